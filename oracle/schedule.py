@@ -1,0 +1,57 @@
+"""Longest-first ordering of query-tile work items (plain definition).
+
+TEST INFRASTRUCTURE (only tests/, ``__graft_entry__.smoke()`` and bench.py's
+``cpu_baseline`` leg may use oracle/).
+
+The method orders its work tiles longest first for causal masks and variable
+lengths (fdeinterviews.com FA4 summary, features paragraph).  A work item is one
+block of ``block_m`` consecutive query rows of one sequence (and one head); its
+length is the number of ``block_n``-key tiles it must visit: all of the
+sequence's key tiles without a mask, and under the causal mask only the tiles
+holding a key at or before the item's last row.
+
+Any order whose costs never increase is a valid longest-first order (equal costs
+may come in any order), so checks compare the multiset of items and the cost
+sequence, and verify monotonicity.
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+
+def item_cost(row0: int, block_m: int, seqlen_q: int, seqlen_k: int, block_n: int,
+              causal: bool) -> int:
+    """Key tiles visited by the query rows [row0, min(row0+block_m, seqlen_q))."""
+    if seqlen_k <= 0:
+        return 0
+    if not causal:
+        keys = seqlen_k
+    else:
+        last_row = min(row0 + block_m, seqlen_q) - 1
+        keys = min(last_row + 1, seqlen_k)
+    return -(-keys // block_n)
+
+
+def work_items(seqlens: Sequence[int], block_m: int, block_n: int,
+               causal: bool) -> List[Tuple[int, int, int]]:
+    """All (sequence, query-tile index, cost) items, in natural order."""
+    items = []
+    for b, length in enumerate(seqlens):
+        length = int(length)
+        for t in range(-(-length // block_m)):
+            items.append((b, t, item_cost(t * block_m, block_m, length, length, block_n, causal)))
+    return items
+
+
+def longest_first(items: Sequence[Tuple[int, int, int]]) -> List[Tuple[int, int, int]]:
+    """One valid longest-first order: stable sort by decreasing cost."""
+    return sorted(items, key=lambda it: -it[2])
+
+
+def is_longest_first(order: Sequence[Tuple[int, int, int]],
+                     items: Sequence[Tuple[int, int, int]]) -> bool:
+    """True if ``order`` is a permutation of ``items`` with non-increasing cost."""
+    if sorted(order) != sorted(items):
+        return False
+    costs = [c for _, _, c in order]
+    return all(a >= b for a, b in zip(costs, costs[1:]))
