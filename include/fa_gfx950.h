@@ -1,0 +1,181 @@
+/*
+ * fa_gfx950.h -- C ABI of the exact tiled attention library for MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention in BF16 as described on
+ * the FlashAttention-4 pages:
+ *   - forward (lecompute.fr FA4 article, section "Between the matrix products the
+ *     kernel must produce weights"; fdeinterviews.com FA4 summary, opening
+ *     paragraph): S = scale * Q K^T, a row softmax P (positive, rows summing to one),
+ *     O = P V, computed tile by tile with an online softmax so that the score matrix
+ *     never exists in device memory; the natural-log log-sum-exp of each row,
+ *     LSE_i = ln sum_j exp(S_ij), is written beside O for the backward;
+ *   - backward (fdeinterviews.com FA4 summary, "Paired-CTA backward pass" bullet and
+ *     features paragraph): dQ, dK, dV from the saved LSE, with dQ accumulated by
+ *     atomic adds or, in deterministic mode, by a fixed-order reduction whose result
+ *     is bit-identical from run to run;
+ *   - causal masks and packed variable-length batches, with work ordered longest
+ *     first (fdeinterviews.com FA4 summary, features paragraph).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP global memory) owned by the caller.
+ *     The library allocates no device memory, keeps no state between calls beyond
+ *     its loaded code object, never synchronizes the host, and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream); all
+ *     device work of a call is enqueued on it, in order.
+ *   - Every argument is validated before any HIP call.  On a non-FA_OK return no
+ *     device work has been enqueued (except FA_ERR_HIP, reported when a launch
+ *     fails).  Faults inside kernels surface asynchronously on the stream.
+ *   - Tensor layouts: fixed length Q/K/V/O/dO are [B, S, H, D] with arbitrary
+ *     element strides for B, S and H (given per tensor) and D contiguous.  Variable
+ *     length tensors are packed [T, H, D] (the batch stride is ignored) with
+ *     sequence b occupying rows cu_seqlens[b] .. cu_seqlens[b+1]-1.
+ *     Base pointers must be 16-byte aligned and the S and H strides multiples of 8
+ *     elements.  bf16 is the IEEE binary32 upper half (bfloat16).
+ *   - LSE is fp32, natural log, with the softmax scale included: [B, H, S_q]
+ *     contiguous for fixed length, [H, total_q] for variable length.
+ *   - cu_seqlens arrays live in device memory, hold batch+1 non-decreasing int32
+ *     entries starting at 0 and ending at total_q (total_k).  Their contents are
+ *     trusted (not validated).  Variable-length causal attention requires equal
+ *     query and key lengths per sequence (cu_seqlens_k == cu_seqlens_q or NULL).
+ *   - Causal masking hides key j from query i when j > i (top-left aligned) and
+ *     requires seqlen_q == seqlen_k.
+ *   - A query row that sees no key gets O = 0 and LSE = -inf.
+ *   - NaN/Inf in the data are propagated, not checked.
+ */
+#ifndef FA_GFX950_H
+#define FA_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride, ... */
+  FA_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,
+  FA_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+} fa_status;
+
+typedef enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype;
+
+/* Arguments of the forward pass. */
+typedef struct fa_fwd_args {
+  const void* q;         /* bf16 [B,S_q,H,D] or [T_q,H,D]                          */
+  const void* k;         /* bf16 [B,S_k,H,D] or [T_k,H,D]                          */
+  const void* v;         /* bf16, same shape as k                                  */
+  void* o;               /* out: bf16, same shape as q                             */
+  float* lse;            /* out: fp32 [B,H,S_q] or [H,T_q]                         */
+  int64_t q_stride[3];   /* element strides {batch, seq, head}                     */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int32_t batch;         /* B (number of sequences for variable length)            */
+  int32_t seqlen_q;      /* S_q (fixed length; ignored when cu_seqlens_q != NULL)  */
+  int32_t seqlen_k;      /* S_k (fixed length)                                     */
+  int32_t num_heads;     /* H (same for Q, K and V)                                */
+  int32_t head_dim;      /* D: 64 or 128                                           */
+  const int32_t* cu_seqlens_q;  /* device, batch+1 entries, or NULL (fixed length) */
+  const int32_t* cu_seqlens_k;  /* device, or NULL (then equal to cu_seqlens_q)    */
+  int32_t max_seqlen_q;  /* variable length: upper bound of any query length      */
+  int32_t max_seqlen_k;
+  int32_t total_q;       /* variable length: T_q = cu_seqlens_q[batch]             */
+  int32_t total_k;
+  float softmax_scale;   /* finite and >= 0, e.g. 1/sqrt(D)                       */
+  int32_t causal;        /* 0 or 1                                                 */
+} fa_fwd_args;
+
+/* Optional forward variant selection (NULL = defaults).  Both knobs select among
+ * compiled kernel instances; values without an instance give FA_ERR_UNSUPPORTED. */
+typedef struct fa_fwd_tuning {
+  /* Of every 16 score registers of a lane, how many take the FMA-only exp2
+   * (integer/fraction split, cubic on the fraction, integer added to the exponent
+   * field; fdeinterviews.com FA4 summary, "Software exponentials" bullet) instead of
+   * the hardware v_exp_f32.  Compiled: 0, 2, 4.  -1 = default. */
+  int32_t exp2_poly_per16;
+  /* Lazy rescale threshold in log2 units (fdeinterviews.com FA4 summary, "Lazy
+   * rescaling" bullet): the output is rescaled only when a row's maximum grows by
+   * more than this.  Compiled: 8 (the method) and 0 (eager).  -1 = default (8). */
+  int32_t rescale_threshold_log2;
+  /* Query tiles of 128 rows interleaved per workgroup (two wave sets sharing each
+   * K/V stage).  Compiled: 1, 2.  -1 = default. */
+  int32_t q_tiles_per_workgroup;
+} fa_fwd_tuning;
+
+/* Bytes of device workspace fa_fwd needs for `a` (0 for fixed length; variable
+ * length needs room for the longest-first work list). */
+fa_status fa_fwd_workspace_size(const fa_fwd_args* a, size_t* bytes);
+
+/* Forward pass: writes O and LSE.  `workspace` (device, 256-byte aligned, at least
+ * fa_fwd_workspace_size bytes, contents ignored on entry) may be NULL when that
+ * size is 0. */
+fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Builds only the longest-first work list of a variable-length forward into
+ * `workspace` (the first step of fa_fwd for variable length), so that it can be
+ * inspected.  Layout: int32 count n, then n pairs {sequence, query tile}, tiles of
+ * `fa_fwd_tile_rows` rows, in dispatch order (each item is run for every head). */
+fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tuning,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Query rows per forward work item for the given tuning (NULL = defaults). */
+int32_t fa_fwd_tile_rows(const fa_fwd_tuning* tuning);
+
+/* Arguments of the backward pass. */
+typedef struct fa_bwd_args {
+  const void* q;         /* bf16, as in the forward                                */
+  const void* k;
+  const void* v;
+  const void* o;         /* bf16 forward output                                    */
+  const void* dout;      /* bf16 gradient of the loss w.r.t. O, shape of o         */
+  const float* lse;      /* fp32 LSE written by fa_fwd (same layout)               */
+  void* dq;              /* out: grad_dtype, shape of q                            */
+  void* dk;              /* out: grad_dtype, shape of k                            */
+  void* dv;              /* out: grad_dtype, shape of v                            */
+  int64_t q_stride[3];   /* element strides {batch, seq, head} of each tensor      */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t do_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  int32_t batch;
+  int32_t seqlen_q;
+  int32_t seqlen_k;
+  int32_t num_heads;
+  int32_t head_dim;      /* 64 or 128 */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int32_t total_q;
+  int32_t total_k;
+  float softmax_scale;
+  int32_t causal;
+  int32_t deterministic; /* 0: dQ by atomic adds; 1: fixed-order, bit-reproducible */
+  int32_t grad_dtype;    /* FA_DTYPE_F32 (default) or FA_DTYPE_BF16                */
+} fa_bwd_args;
+
+/* Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, row terms
+ * D_i = sum_d dO_id O_id, work lists). */
+fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes);
+
+/* Backward pass: writes dQ, dK, dV.  `workspace` as for fa_fwd (required). */
+fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Library version string. */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_GFX950_H */

@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU parity tests: device upload of the seeded bf16 inputs,
+oracle evaluation on sampled heads/rows, and error metrics."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as OA
+from tiled_exact_attention_bf16_amd import inputs as I
+
+# Tolerances on O, dQ, dK, dV (max-abs and mean-abs) and LSE (max-abs) against the fp64 oracle.
+TOL_MAX = 1e-2
+TOL_MEAN = 1e-3
+TOL_LSE = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def upload(inp: I.AttnInputs):
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    do = dev_bf16(inp.do) if inp.do is not None else None
+    cu = torch.from_numpy(inp.cu_seqlens).cuda() if inp.varlen else None
+    return q, k, v, do, cu
+
+
+def bf16_rounding_floor(ref: np.ndarray) -> float:
+    """Mean |bf16(ref) - ref|: the error a bf16 output carries from its own rounding.
+
+    The five named workloads use the literal mean-abs bar; edge-case shapes (a
+    handful of keys, so outputs are O(1) and not averaged down) add this floor to
+    it, since no bf16 output can do better than the oracle rounded to bf16."""
+    r32 = ref.astype(np.float32)
+    rounded = I.bf16_bits_to_f32(I.f32_to_bf16_bits(r32)).astype(np.float64)
+    return float(np.abs(rounded - ref).mean()) if ref.size else 0.0
+
+
+def bf16_rounding_max(ref: np.ndarray) -> float:
+    """Max |bf16(ref) - ref| (half a bf16 ulp of the largest elements)."""
+    r32 = ref.astype(np.float32)
+    rounded = I.bf16_bits_to_f32(I.f32_to_bf16_bits(r32)).astype(np.float64)
+    return float(np.abs(rounded - ref).max()) if ref.size else 0.0
+
+
+def errors(gpu: np.ndarray, ref: np.ndarray):
+    d = np.abs(gpu.astype(np.float64) - ref)
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def lse_error(gpu: np.ndarray, ref: np.ndarray):
+    gpu = gpu.astype(np.float64)
+    both_inf = np.isneginf(gpu) & np.isneginf(ref)
+    d = np.where(both_inf, 0.0, np.abs(gpu - ref))
+    return float(np.nanmax(d)) if d.size else 0.0
+
+
+def head_slices(inp: I.AttnInputs, b: int, h: int, name: str):
+    """float64 [L, D] view of one sequence and head of a tensor."""
+    return I.bf16_bits_to_f64(inp.sequence(b, name)[:, h])
+
+
+def oracle_fwd_head(inp: I.AttnInputs, b: int, h: int, rows=None):
+    q, k, v = (head_slices(inp, b, h, t) for t in ("q", "k", "v"))
+    return OA.head_forward(q, k, v, inp.scale, inp.causal, rows=rows)
+
+
+def oracle_bwd_head(inp: I.AttnInputs, b: int, h: int):
+    q, k, v, do = (head_slices(inp, b, h, t) for t in ("q", "k", "v", "do"))
+    return OA.head_backward(q, k, v, do, inp.scale, inp.causal)
+
+
+def gpu_head(t: torch.Tensor, inp: I.AttnInputs, b: int, h: int) -> np.ndarray:
+    """[L, D] slice of a GPU output tensor (same layout as the inputs), as float64 numpy."""
+    if inp.varlen:
+        s0, s1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        x = t[s0:s1, h]
+    else:
+        x = t[b, :, h]
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def gpu_lse_head(lse: torch.Tensor, inp: I.AttnInputs, b: int, h: int) -> np.ndarray:
+    if inp.varlen:
+        s0, s1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        return lse[h, s0:s1].cpu().numpy().astype(np.float64)
+    return lse[b, h].cpu().numpy().astype(np.float64)

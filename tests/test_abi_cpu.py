@@ -1,0 +1,202 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments before touching the GPU (CPU only: no compute calls are made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_exact_attention_bf16_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_gfx950.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="library not built")
+
+P = 0x100000  # aligned stand-in device addresses; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = L.lib()
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    for code, name in [(0, "FA_OK"), (1, "FA_ERR_INVALID_ARGUMENT"), (2, "FA_ERR_UNSUPPORTED"),
+                       (3, "FA_ERR_WORKSPACE_TOO_SMALL"), (4, "FA_ERR_HIP")]:
+        assert L.status_str(code) == name
+    assert L.lib().fa_version().startswith(b"fa_gfx950")
+
+
+def fwd_args(b=2, s=256, h=4, d=128, causal=0, scale=0.088):
+    a = L.FwdArgs()
+    a.q, a.k, a.v, a.o, a.lse = P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000
+    st = L.Strides(s * h * d, h * d, d)
+    a.q_stride = a.k_stride = a.v_stride = a.o_stride = st
+    a.batch, a.seqlen_q, a.seqlen_k, a.num_heads, a.head_dim = b, s, s, h, d
+    a.softmax_scale, a.causal = scale, causal
+    return a
+
+
+def ws_size(a):
+    n = ctypes.c_size_t(123)
+    st = L.lib().fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def fwd_status(a, tuning=None, ws=None, ws_bytes=0):
+    t = tuning if tuning is not None else L.FwdTuning(-1, -1, -1)
+    return L.lib().fa_fwd(ctypes.byref(a), ctypes.byref(t), ws, ws_bytes, None)
+
+
+def test_fixed_length_forward_needs_no_workspace():
+    assert ws_size(fwd_args()) == (L.FA_OK, 0)
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda a: setattr(a, "q", None), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "lse", None), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "k", P + 8), L.FA_ERR_INVALID_ARGUMENT),          # misaligned
+    (lambda a: setattr(a, "head_dim", 96), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "head_dim", 0), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "num_heads", 0), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "batch", -1), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "seqlen_q", -5), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "softmax_scale", float("nan")), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "softmax_scale", float("inf")), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "softmax_scale", -1.0), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "causal", 2), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: (setattr(a, "causal", 1), setattr(a, "seqlen_k", 128)), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "q_stride", L.Strides(256 * 512, 500, 128)), L.FA_ERR_INVALID_ARGUMENT),  # stride % 8
+    (lambda a: setattr(a, "o_stride", L.Strides(256 * 512, 64, 128)), L.FA_ERR_INVALID_ARGUMENT),   # rows overlap D
+    (lambda a: setattr(a, "cu_seqlens_k", P), L.FA_ERR_INVALID_ARGUMENT),   # k offsets without q offsets
+    (lambda a: setattr(a, "v_stride", L.Strides(0, 1 << 24, 128)), L.FA_ERR_UNSUPPORTED),  # 32-bit offsets
+])
+def test_forward_validation(mutate, expect):
+    a = fwd_args()
+    mutate(a)
+    assert fwd_status(a) == expect
+    assert ws_size(a)[0] == expect
+
+
+@pytest.mark.parametrize("tuning,expect", [
+    ((3, -1, -1), L.FA_ERR_UNSUPPORTED),
+    ((2, 0, -1), L.FA_ERR_UNSUPPORTED),
+    ((-1, 5, -1), L.FA_ERR_UNSUPPORTED),
+    ((-1, -1, 3), L.FA_ERR_UNSUPPORTED),
+])
+def test_forward_tuning_validation(tuning, expect):
+    assert fwd_status(fwd_args(), L.FwdTuning(*tuning)) == expect
+
+
+def test_tile_rows():
+    lib = L.lib()
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 1))) == 128
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 2))) == 256
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 7))) == 0
+
+
+def varlen_args(n_seq=32, total=131072, max_len=16384, causal=1, h=16, d=128):
+    a = fwd_args(b=n_seq, h=h, d=d, causal=causal)
+    a.cu_seqlens_q = P + 0x5000000
+    a.total_q = a.total_k = total
+    a.max_seqlen_q = a.max_seqlen_k = max_len
+    st = L.Strides(0, h * d, d)
+    a.q_stride = a.k_stride = a.v_stride = a.o_stride = st
+    return a
+
+
+def test_varlen_workspace_and_checks():
+    a = varlen_args()
+    st, n = ws_size(a)
+    assert st == L.FA_OK
+    items = (131072 + 127) // 128 + 32
+    assert n >= 4 * (1 + 2 * items) and n % 256 == 0
+    assert fwd_status(a, ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert fwd_status(a, L.FwdTuning(-1, -1, 1), ws=P, ws_bytes=n - 256) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert fwd_status(a, ws=P + 16, ws_bytes=n) == L.FA_ERR_INVALID_ARGUMENT  # workspace alignment
+    a.cu_seqlens_k = P + 0x6000000                                          # causal needs shared offsets
+    assert fwd_status(a) == L.FA_ERR_UNSUPPORTED
+    b = varlen_args()
+    b.cu_seqlens_q = P + 2                                                   # int32 alignment
+    assert ws_size(b)[0] == L.FA_ERR_INVALID_ARGUMENT
+    c = varlen_args(max_len=1 << 20)                                         # longest-first histogram range
+    assert ws_size(c)[0] == L.FA_ERR_UNSUPPORTED
+    d = varlen_args()
+    d.max_seqlen_q = -1
+    assert ws_size(d)[0] == L.FA_ERR_INVALID_ARGUMENT
+
+
+def test_build_schedule_rejects_fixed_length_and_small_workspace():
+    lib = L.lib()
+    t = L.FwdTuning(-1, -1, -1)
+    assert lib.fa_fwd_build_schedule(ctypes.byref(fwd_args()), ctypes.byref(t), P, 1 << 20, None) == \
+        L.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_fwd_build_schedule(ctypes.byref(varlen_args()), ctypes.byref(t), P, 64, None) == \
+        L.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+def bwd_args(b=2, s=256, h=4, d=128, causal=1, det=0, gd=L.FA_DTYPE_F32):
+    a = L.BwdArgs()
+    for i, f in enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"]):
+        setattr(a, f, P + i * 0x1000000)
+    st = L.Strides(s * h * d, h * d, d)
+    for f in ["q", "k", "v", "o", "do", "dq", "dk", "dv"]:
+        setattr(a, f + "_stride", st)
+    a.batch, a.seqlen_q, a.seqlen_k, a.num_heads, a.head_dim = b, s, s, h, d
+    a.softmax_scale, a.causal, a.deterministic, a.grad_dtype = 0.088, causal, det, gd
+    return a
+
+
+def bwd_ws(a):
+    n = ctypes.c_size_t(0)
+    return L.lib().fa_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_backward_workspace_sizes():
+    st, n_atomic = bwd_ws(bwd_args(det=0))
+    assert st == L.FA_OK
+    rows = 2 * 256 * 4
+    assert n_atomic >= rows * 128 * 4 + rows * 4          # fp32 dQ accumulator + row terms
+    st, n_det = bwd_ws(bwd_args(det=1))
+    assert st == L.FA_OK and rows * 4 <= n_det < n_atomic  # no accumulator in deterministic mode
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda a: setattr(a, "dout", None), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "dq", P + 4), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "deterministic", 3), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "grad_dtype", 7), L.FA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "head_dim", 256), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "seqlen_k", 100), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dk_stride", L.Strides(256 * 512, 130, 128)), L.FA_ERR_INVALID_ARGUMENT),
+])
+def test_backward_validation(mutate, expect):
+    a = bwd_args()
+    mutate(a)
+    assert bwd_ws(a)[0] == expect
+    assert L.lib().fa_bwd(ctypes.byref(a), P, 1 << 30, None) == expect
+
+
+def test_backward_workspace_too_small():
+    a = bwd_args()
+    st, n = bwd_ws(a)
+    assert L.lib().fa_bwd(ctypes.byref(a), P, n - 1, None) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert L.lib().fa_bwd(ctypes.byref(a), None, 0, None) == L.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(L.FaLibraryMissing):
+        L.lib()

@@ -1,0 +1,93 @@
+"""Backward parity (atomic and deterministic dQ) against the fp64 oracle, and the
+deterministic mode's bitwise reproducibility."""
+import numpy as np
+import pytest
+import torch
+
+from tiled_exact_attention_bf16_amd import inputs as I
+from tests.gpu_util import (TOL_MAX, TOL_MEAN, bf16_rounding_floor, bf16_rounding_max, errors, gpu_head,
+                            oracle_bwd_head, say, upload)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tiled_exact_attention_bf16_amd import attention as FA
+
+
+def run_fwd_bwd(inp, deterministic, grad_dtype=torch.float32):
+    q, k, v, do, cu = upload(inp)
+    ms = inp.max_seqlen() if inp.varlen else None
+    o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=ms)
+    dq, dk, dv = FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, deterministic=deterministic,
+                        grad_dtype=grad_dtype, cu_seqlens_q=cu, max_seqlen_q=ms)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_grads(inp, grads, pairs, tag, strict=False):
+    """strict: the literal bar (named workloads); bf16 gradient outputs may add their own rounding floor."""
+    worst = {}
+    for b, h in pairs:
+        ref = oracle_bwd_head(inp, b, h)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            got = gpu_head(g, inp, b, h)
+            assert np.all(np.isfinite(got)), (tag, name, b, h)
+            mx, mean = errors(got, r)
+            w = worst.get(name, (0.0, 0.0))
+            worst[name] = (max(w[0], mx), max(w[1], mean))
+            relax = g.dtype == torch.bfloat16 and not strict
+            floor_max = bf16_rounding_max(r) if relax else 0.0
+            floor_mean = bf16_rounding_floor(r) if relax else 0.0
+            assert mx <= TOL_MAX + floor_max and mean <= TOL_MEAN + floor_mean, (tag, name, b, h, mx, mean)
+    say(f"[bwd {tag}] " + "  ".join(f"{k} {v[0]:.3e}/{v[1]:.3e}" for k, v in worst.items()))
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("s", [1, 17, 128, 129, 300, 1000])
+def test_small_shapes(s, causal, d, deterministic):
+    inp = I.random_inputs(200 + s, 2, s, 2, d, causal, with_do=True)
+    say(f"case s={s} causal={causal} d={d} det={deterministic}")
+    grads = run_fwd_bwd(inp, deterministic)
+    check_grads(inp, grads, [(b, h) for b in range(2) for h in range(2)], f"s{s}c{int(causal)}d{d}det{int(deterministic)}")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_varlen_ragged(deterministic):
+    lens = [0, 1, 5, 128, 129, 300, 17, 0, 256, 511]
+    inp = I.random_varlen_inputs(12, lens, heads=2, head_dim=128, causal=True, with_do=True)
+    say(f"case varlen det={deterministic}")
+    grads = run_fwd_bwd(inp, deterministic)
+    check_grads(inp, grads, [(b, h) for b in range(len(lens)) for h in range(2)], f"varlen det{int(deterministic)}")
+
+
+def test_bf16_gradient_outputs():
+    inp = I.random_inputs(300, 1, 512, 2, 128, True, with_do=True)
+    grads = run_fwd_bwd(inp, False, grad_dtype=torch.bfloat16)
+    assert all(g.dtype == torch.bfloat16 for g in grads)
+    check_grads(inp, grads, [(0, 0), (0, 1)], "bf16-out")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_config_c5_sampled_heads(deterministic):
+    inp = I.make_inputs("c5")
+    say(f"case c5 det={deterministic}")
+    grads = run_fwd_bwd(inp, deterministic)
+    for g in grads:
+        assert bool(torch.isfinite(g).all())
+    check_grads(inp, grads, [(0, 0), (1, 15)], f"c5 det{int(deterministic)}", strict=True)
+
+
+def test_deterministic_mode_is_bitwise_reproducible():
+    inp = I.make_inputs("c5")
+    q, k, v, do, _ = upload(inp)
+    o, lse = FA.fwd(q, k, v, inp.scale, True)
+    first = FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=True)
+    first = [g.clone() for g in first]
+    for rep in range(5):
+        again = FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=True)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+    say("[deterministic] 5 repeats bitwise identical on c5")

@@ -1,0 +1,179 @@
+"""Thin torch binding of the C ABI (argument marshalling only).
+
+torch supplies device memory and the current HIP stream; every step of the
+attention computation runs in the library's gfx950 kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class Tuning:
+    """Forward variant: FMA-exp2 share (of 16), lazy threshold (log2 units), query tiles per workgroup.
+    -1 keeps the library default."""
+    exp2_poly_per16: int = -1
+    rescale_threshold_log2: int = -1
+    q_tiles_per_workgroup: int = -1
+
+    def c(self):
+        return L.FwdTuning(self.exp2_poly_per16, self.rescale_threshold_log2, self.q_tiles_per_workgroup)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t: torch.Tensor, varlen: bool):
+    if t.stride(-1) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if varlen:
+        if t.dim() != 3:
+            raise ValueError("packed variable-length tensors are [T, H, D]")
+        return L.Strides(0, t.stride(0), t.stride(1))
+    if t.dim() != 4:
+        raise ValueError("fixed-length tensors are [B, S, H, D]")
+    return L.Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _max_len(cu: torch.Tensor) -> int:
+    # host copy of the lengths (a synchronisation); pass max_seqlen to avoid it
+    return int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+
+
+def fwd_args(q, k, v, o, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None) -> L.FwdArgs:
+    varlen = cu_seqlens_q is not None
+    a = L.FwdArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
+    a.q_stride, a.k_stride = _strides(q, varlen), _strides(k, varlen)
+    a.v_stride, a.o_stride = _strides(v, varlen), _strides(o, varlen)
+    a.num_heads, a.head_dim = q.shape[-2], q.shape[-1]
+    a.softmax_scale = softmax_scale
+    a.causal = int(bool(causal))
+    if varlen:
+        a.batch = cu_seqlens_q.numel() - 1
+        a.cu_seqlens_q = _ptr(cu_seqlens_q)
+        a.cu_seqlens_k = _ptr(cu_seqlens_k) if cu_seqlens_k is not None else None
+        a.total_q, a.total_k = q.shape[0], k.shape[0]
+        a.max_seqlen_q = _max_len(cu_seqlens_q) if max_seqlen_q is None else max_seqlen_q
+        if cu_seqlens_k is None:
+            a.max_seqlen_k = a.max_seqlen_q
+        else:
+            a.max_seqlen_k = _max_len(cu_seqlens_k) if max_seqlen_k is None else max_seqlen_k
+    else:
+        a.batch, a.seqlen_q, a.seqlen_k = q.shape[0], q.shape[1], k.shape[1]
+    return a
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Optional[float] = None,
+        causal: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,
+        cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+        max_seqlen_k: Optional[int] = None, tuning: Optional[Tuning] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention forward.  Returns (O bf16 like q, LSE fp32 [B,H,S] or [H,T])."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    varlen = cu_seqlens_q is not None
+    if out is None:
+        out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        shape = (q.shape[1], q.shape[0]) if varlen else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    a = fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    lib = L.lib()
+    need = ctypes.c_size_t(0)
+    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_fwd_workspace_size")
+    if need.value > 0 and (workspace is None or workspace.numel() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    t = (tuning or Tuning()).c()
+    L.check(lib.fa_fwd(ctypes.byref(a), ctypes.byref(t), _ptr(workspace) if need.value else None,
+                       need.value, _stream(stream)), "fa_fwd")
+    return out, lse
+
+
+def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[Tuning] = None, stream=None):
+    """Runs only the variable-length longest-first list builder; returns (tile_rows, [(seq, tile), ...])."""
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    a = fwd_args(q, k, k, o, lse, 1.0, causal, cu_seqlens, None, max_seqlen, None)
+    lib = L.lib()
+    need = ctypes.c_size_t(0)
+    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_fwd_workspace_size")
+    ws = torch.zeros(max(need.value, 256), dtype=torch.uint8, device=q.device)
+    t = (tuning or Tuning()).c()
+    L.check(lib.fa_fwd_build_schedule(ctypes.byref(a), ctypes.byref(t), _ptr(ws), ws.numel(), _stream(stream)),
+            "fa_fwd_build_schedule")
+    words = ws.view(torch.int32).cpu()
+    n = int(words[0])
+    items = [(int(words[1 + 2 * i]), int(words[2 + 2 * i])) for i in range(n)]
+    return int(lib.fa_fwd_tile_rows(ctypes.byref(t))), items
+
+
+def bwd_args(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale, causal, deterministic, grad_dtype,
+             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None) -> L.BwdArgs:
+    varlen = cu_seqlens_q is not None
+    a = L.BwdArgs()
+    a.q, a.k, a.v, a.o, a.dout, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse)
+    a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    a.q_stride, a.k_stride, a.v_stride = _strides(q, varlen), _strides(k, varlen), _strides(v, varlen)
+    a.o_stride, a.do_stride = _strides(o, varlen), _strides(dout, varlen)
+    a.dq_stride, a.dk_stride, a.dv_stride = _strides(dq, varlen), _strides(dk, varlen), _strides(dv, varlen)
+    a.num_heads, a.head_dim = q.shape[-2], q.shape[-1]
+    a.softmax_scale = softmax_scale
+    a.causal = int(bool(causal))
+    a.deterministic = int(bool(deterministic))
+    a.grad_dtype = L.FA_DTYPE_F32 if grad_dtype == torch.float32 else L.FA_DTYPE_BF16
+    if varlen:
+        a.batch = cu_seqlens_q.numel() - 1
+        a.cu_seqlens_q = _ptr(cu_seqlens_q)
+        a.cu_seqlens_k = _ptr(cu_seqlens_k) if cu_seqlens_k is not None else None
+        a.total_q, a.total_k = q.shape[0], k.shape[0]
+        a.max_seqlen_q = _max_len(cu_seqlens_q) if max_seqlen_q is None else max_seqlen_q
+        if cu_seqlens_k is None:
+            a.max_seqlen_k = a.max_seqlen_q
+        else:
+            a.max_seqlen_k = _max_len(cu_seqlens_k) if max_seqlen_k is None else max_seqlen_k
+    else:
+        a.batch, a.seqlen_q, a.seqlen_k = q.shape[0], q.shape[1], k.shape[1]
+    return a
+
+
+def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+        lse: torch.Tensor, softmax_scale: Optional[float] = None, causal: bool = False,
+        deterministic: bool = False, grad_dtype: torch.dtype = torch.float32,
+        cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+        max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Exact attention backward from the saved LSE.  Returns (dQ, dK, dV) in grad_dtype."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_dtype must be float32 or bfloat16")
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device) if dv is None else dv
+    a = bwd_args(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale, causal, deterministic, grad_dtype,
+                 cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    lib = L.lib()
+    need = ctypes.c_size_t(0)
+    L.check(lib.fa_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_bwd_workspace_size")
+    if need.value > 0 and (workspace is None or workspace.numel() < need.value):
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    L.check(lib.fa_bwd(ctypes.byref(a), _ptr(workspace) if need.value else None, need.value, _stream(stream)),
+            "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,90 @@
+// Internal interface between the C-ABI layer (fa_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Geometry shared by host and device code.
+constexpr int kFwdTileRows = 128;  // query rows per tile (4 waves x 32 rows)
+constexpr int kFwdBlockN = 64;     // keys per K/V stage in the forward
+constexpr int kBwdBlockN = 128;    // keys per backward work item (4 waves x 32 keys)
+constexpr int kBwdBlockM = 64;     // query rows per backward step
+constexpr int kSchedMaxCost = 8192;  // histogram bins of the longest-first sort
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int batch, seqlen_q, seqlen_k, heads;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q;
+  int n_qtiles;        // fixed length: work items per (batch, head)
+  const int32_t* sched;  // variable length: {count, (seq, tile) pairs...}
+  float scale;         // softmax scale
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+struct FwdConfig {
+  int head_dim;     // 64 or 128
+  int q_tiles;      // 1 or 2 query tiles per workgroup
+  bool causal;
+  bool varlen;
+  int poly_per16;   // 0, 2, 4
+  int tau;          // 8 or 0
+};
+
+// Returns hipSuccess or the launch error.  Grid size is derived from p and cfg.
+hipError_t launch_fwd(const FwdParams& p, const FwdConfig& cfg, hipStream_t stream);
+
+// Builds the longest-first list {count, (seq, tile)...} for variable length.
+hipError_t launch_fwd_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int tile_rows,
+                               int block_n, bool causal, int32_t* out, hipStream_t stream);
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int batch, seqlen_q, seqlen_k, heads;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
+  int max_seqlen_q, max_seqlen_k;
+  float scale;
+  float scale_log2;
+  bool causal;
+  bool varlen;
+  bool deterministic;
+  bool grad_bf16;
+  int head_dim;
+  // workspace carve-up
+  float* dq_acc;      // [H, total_q, D] fp32 (fixed length: total_q = B*S_q)
+  float* dvec;        // [H, total_q] fp32, D_i = sum_d dO_id O_id
+  int32_t* sched;     // variable length work list for the key-tile kernel
+};
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fa
