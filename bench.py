@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (BF16) on one MI355X.
+
+One step = the whole hot path on one batch: fa_fwd (O, LSE) then fa_bwd (dQ, dK,
+dV, atomic dQ) on the causal B=2, H=16, S=8192, d=128 workload (synthetic
+normal inputs, already resident in HBM).  Throughput counts algorithmic FLOP:
+4*d per visible (query, key) pair forward and 10*d backward, causal pairs only.
+
+Prints one JSON line.  Per-kernel average durations come from HIP events on the
+stream the library launches on (torch's current stream); the roofline object
+describes the kernel with the largest share of the step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "headline"       # causal B=2 H=16 S=8192 d=128
+BWD_SEED_CONFIG = "c5"      # same shape with dO
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, budget_s: float = 12.0, max_heads: int = 8):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    forward then backward of whole (sequence, head) pairs, until ``budget_s``."""
+    from oracle import attention as OA
+    from tiled_exact_attention_bf16_amd import inputs as I
+    from tiled_exact_attention_bf16_amd import workload as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    done, t_total, flop = 0, 0.0, 0
+    pairs = [(b, h) for b in range(inp.batch) for h in range(inp.num_heads)]
+    for b, h in pairs[:max_heads]:
+        q, k, v, do = (I.bf16_bits_to_f64(inp.sequence(b, t)[:, h]) for t in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        OA.head_forward(q, k, v, inp.scale, inp.causal)
+        OA.head_backward(q, k, v, do, inp.scale, inp.causal)
+        t_total += time.perf_counter() - t0
+        s = q.shape[0]
+        flop += W.fwd_flops([s], [s], 1, q.shape[1], inp.causal) + W.bwd_flops([s], [s], 1, q.shape[1], inp.causal)
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(flop / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy forward+backward of {done} whole (sequence, head) pairs of the "
+                      f"{inp.q.shape[1]}-token causal workload, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deterministic", action="store_true", help="time the deterministic backward")
+    ap.add_argument("--q-tiles", type=int, default=-1)
+    ap.add_argument("--poly", type=int, default=-1)
+    ap.add_argument("--tau", type=int, default=-1)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_exact_attention_bf16_amd import _lib as L
+    from tiled_exact_attention_bf16_amd import attention as FA
+    from tiled_exact_attention_bf16_amd import inputs as I
+    from tiled_exact_attention_bf16_amd import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    L.lib()  # fail loudly if the HIP library is missing
+
+    inp = I.make_inputs(BWD_SEED_CONFIG)   # B=2 S=8192 H=16 d=128 causal, with dO
+    B, S, H, D = inp.q.shape
+    log(f"[bench] workload causal B={B} S={S} H={H} d={D}; uploading")
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.do)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")   # >= the backward's accumulator
+    tuning = FA.Tuning(args.poly, args.tau, args.q_tiles)
+    det = args.deterministic
+
+    def fwd():
+        FA.fwd(q, k, v, inp.scale, True, tuning=tuning, out=o, lse=lse)
+
+    def bwd(phases=L.FA_BWD_PHASE_ALL):
+        FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=det, dq=dq, dk=dk, dv=dv, workspace=ws,
+               phases=phases)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # per-kernel events on the library's stream (torch's current stream)
+    names = ["fwd", "bwd_pre", "bwd_main", "bwd_post"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record()
+        fwd()
+        e[1].record()
+        bwd(L.FA_BWD_PHASE_PRE)
+        e[2].record()
+        bwd(L.FA_BWD_PHASE_MAIN)
+        e[3].record()
+        if not det:
+            bwd(L.FA_BWD_PHASE_POST)
+        e[4].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+           for j, n in enumerate(names)}
+    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)]))
+
+    seq = [S] * B
+    f_fwd = W.fwd_flops(seq, seq, H, D, True)
+    f_bwd = W.bwd_flops(seq, seq, H, D, True)
+    fwd_tf = f_fwd / (per["fwd"] * 1e-3) / 1e12
+    bwd_ms = per["bwd_pre"] + per["bwd_main"] + per["bwd_post"]
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    dominant = max(("fwd", "bwd_main"), key=lambda n: per[n])
+    dom_flop = f_fwd if dominant == "fwd" else f_bwd
+    achieved = dom_flop / (per[dominant] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fa::fwd_kernel<128,2,causal>", "bwd_main": "fa::bwd_kv_kernel<128,causal,atomic>"
+                    if not det else "fa::bwd_kv_kernel + fa::bwd_dq_kernel"}
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (BF16, d=128, causal S=8K) and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal attention forward+backward, B=2 H=16 S=8192 d=128 (bf16 in, fp32 grads, "
+                               + ("deterministic" if det else "atomic") + " dQ)",
+                   "global_batch": B, "seq_len": S, "heads": H, "head_dim": D, "causal": True,
+                   "parallelism": "single-gpu"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(bwd_tf, 2),
+        "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {n: round(per[n], 4) for n in names},
+        "roofline": {"bound": "mfma", "kernel": kernel_names[dominant], "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,6 +168,20 @@ fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes);
 /* Backward pass: writes dQ, dK, dV.  `workspace` as for fa_fwd (required). */
 fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward's three phases, enqueued in this order by fa_bwd:
+ *   FA_BWD_PHASE_PRE:  row terms D_i = sum_d dO_id O_id into the workspace (and, in
+ *                      atomic mode, zeroing of the fp32 dQ accumulator);
+ *   FA_BWD_PHASE_MAIN: the gradient products (dK, dV; dQ by atomics into the
+ *                      accumulator, or directly in deterministic mode);
+ *   FA_BWD_PHASE_POST: atomic mode only: dQ from the accumulator in dQ's layout/dtype.
+ * fa_bwd_phases runs the selected subset (a bitwise OR) on the same arguments and
+ * workspace, so callers can time or interleave them; a phase reads what the earlier
+ * phases left in the workspace, so running MAIN without a preceding PRE on that
+ * workspace gives undefined gradients. */
+enum { FA_BWD_PHASE_PRE = 1, FA_BWD_PHASE_MAIN = 2, FA_BWD_PHASE_POST = 4, FA_BWD_PHASE_ALL = 7 };
+fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

@@ -16,6 +16,10 @@ FA_ERR_INVALID_ARGUMENT = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_WORKSPACE_TOO_SMALL = 3
 FA_ERR_HIP = 4
+FA_BWD_PHASE_PRE = 1
+FA_BWD_PHASE_MAIN = 2
+FA_BWD_PHASE_POST = 4
+FA_BWD_PHASE_ALL = 7
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F32 = 1
 
@@ -74,6 +78,7 @@ SIGNATURES = {
     "fa_fwd_tile_rows": (c_int32, [POINTER(FwdTuning)]),
     "fa_bwd_workspace_size": (c_int32, [POINTER(BwdArgs), POINTER(c_size_t)]),
     "fa_bwd": (c_int32, [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
+    "fa_bwd_phases": (c_int32, [POINTER(BwdArgs), c_int32, c_void_p, c_size_t, c_void_p]),
     "fa_status_str": (c_char_p, [c_int32]),
     "fa_version": (c_char_p, []),
 }

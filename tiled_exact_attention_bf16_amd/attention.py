@@ -158,8 +158,11 @@ def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
         cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
         max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
         dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None, stream=None):
-    """Exact attention backward from the saved LSE.  Returns (dQ, dK, dV) in grad_dtype."""
+        workspace: Optional[torch.Tensor] = None, stream=None, phases: int = L.FA_BWD_PHASE_ALL):
+    """Exact attention backward from the saved LSE.  Returns (dQ, dK, dV) in grad_dtype.
+
+    ``phases`` selects a subset of the backward's kernels (fa_bwd_phases); the
+    default runs all of them."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     if grad_dtype not in (torch.float32, torch.bfloat16):
@@ -174,6 +177,10 @@ def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
     L.check(lib.fa_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_bwd_workspace_size")
     if need.value > 0 and (workspace is None or workspace.numel() < need.value):
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    L.check(lib.fa_bwd(ctypes.byref(a), _ptr(workspace) if need.value else None, need.value, _stream(stream)),
-            "fa_bwd")
+    if phases == L.FA_BWD_PHASE_ALL:
+        L.check(lib.fa_bwd(ctypes.byref(a), _ptr(workspace) if need.value else None, need.value, _stream(stream)),
+                "fa_bwd")
+    else:
+        L.check(lib.fa_bwd_phases(ctypes.byref(a), phases, _ptr(workspace) if need.value else None, need.value,
+                                  _stream(stream)), "fa_bwd_phases")
     return dq, dk, dv

@@ -283,6 +283,12 @@ fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes) {
 }
 
 fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_phases(a, FA_BWD_PHASE_ALL, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (phases <= 0 || (phases & ~FA_BWD_PHASE_ALL)) return FA_ERR_INVALID_ARGUMENT;
   Shape s;
   fa_status st = check_bwd(a, &s);
   if (st != FA_OK) return st;
@@ -324,7 +330,7 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, 
   p.dq_acc = a->deterministic ? nullptr : (float*)(ws + lay.dq_acc);
   p.dvec = (float*)(ws + lay.dvec);
   p.sched = s.varlen ? (int32_t*)(ws + lay.sched) : nullptr;
-  return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa::launch_bwd(p, phases, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -648,10 +648,10 @@ __global__ __launch_bounds__(1024) void sched_kv_kernel(const int32_t* cu_q, con
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t stream) {
   const bool atomic = !p.deterministic;
   const int64_t rows = (int64_t)p.total_q * p.heads;
-  {
+  if (phases & 1) {
     int64_t work = rows * (D / 8);
     int grid = (int)std::min<int64_t>((work + 255) / 256, 2048 * 4);
     if (grid < 1) grid = 1;
@@ -660,7 +660,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   // key-block kernel
-  {
+  if (phases & 2) {
     unsigned grid;
     if (p.varlen) {
       hipError_t e = hipSuccess;
@@ -687,6 +687,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     }
   }
   if (atomic) {
+    if (!(phases & 4)) return hipSuccess;
     int64_t work = rows * (D / 4);
     int grid = (int)std::min<int64_t>((work + 255) / 256, 2048 * 4);
     if (grid < 1) grid = 1;
@@ -694,6 +695,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
   }
   // deterministic: query-major dQ kernel; its list reuses the forward's query-tile order
+  if (!(phases & 2)) return hipSuccess;
   unsigned grid;
   int32_t* qsched = p.sched + 1 + 2 * ((p.total_k + kBwdBlockN - 1) / kBwdBlockN + p.batch);
   if (p.varlen) {
@@ -713,8 +715,8 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  return p.head_dim == 128 ? launch_bwd_d<128>(p, stream) : launch_bwd_d<64>(p, stream);
+hipError_t launch_bwd(const BwdParams& p, int phases, hipStream_t stream) {
+  return p.head_dim == 128 ? launch_bwd_d<128>(p, phases, stream) : launch_bwd_d<64>(p, phases, stream);
 }
 
 }  // namespace fa

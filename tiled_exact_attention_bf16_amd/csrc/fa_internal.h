@@ -85,6 +85,6 @@ struct BwdParams {
   int32_t* sched;     // variable length work list for the key-tile kernel
 };
 
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int phases, hipStream_t stream);  // phases: 1 pre, 2 main, 4 post
 
 }  // namespace fa
