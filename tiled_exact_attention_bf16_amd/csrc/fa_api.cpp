@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fa_gfx950.h"
+#include "fa_gfx950.h"
 #include "fa_internal.h"
 
 namespace {

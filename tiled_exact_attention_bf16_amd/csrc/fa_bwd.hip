@@ -160,25 +160,59 @@ __device__ __forceinline__ void store_grad4(rsrc_t r, uint32_t byte_off_f32, uin
 
 // ---------------------------------------------------------------------------
 // bwd_kv: dK, dV (and atomic dQ) for one block of 128 keys.
+//
+// Eight waves, two per SIMD: wave w owns the 32 keys k_blk0 + 32*(w&3) + (lane&31)
+// and, of every 64-row query step, the 32-row half w>>2.  The two waves of a SIMD
+// therefore work on the same keys with independent rows, which lets the hardware
+// overlap one wave's softmax arithmetic with the other's matrix products; each keeps
+// a partial dK^T/dV^T that is summed through LDS at the end.  K and V stay in LDS
+// (row reads feed S = Q K^T and dP = dO V^T; transpose reads feed dQ = dS K).
+//
+// Per step and wave:
+//   S = Q K^T, dP = dO V^T       (C layout: lane = key, registers = 16 query rows)
+//   P = 2^(S*c - LSE*log2 e),  dS' = scale * P (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T [dS'_hi; dS'_lo]   (A operands by transpose reads)
+// Atomic mode: dS'^T (hi, lo) goes to LDS; after a barrier each wave computes one
+// 32x32 block of dQ = dS' K and adds it with fp32 buffer atomics (rows past the end
+// are dropped by the buffer range check).
+//
+// The Q/dO stage is single-buffered: the next step's DMA is issued after the second
+// barrier (once every wave has finished reading the stage) and overlaps the dQ part.
+//
+// dS'^T LDS layout: [128 keys][64 queries] bf16, 128-byte rows of sixteen 8-byte
+// granules; granule g of row r is stored at g ^ ds_swizzle(r), which keeps both the
+// 32-row column writes and the 4-row transpose reads free of bank conflicts.
+__device__ __forceinline__ int ds_swizzle(int row) { return (((row >> 1) & 3) << 2) | ((row >> 3) & 3); }
+
 template <int D, bool CAUSAL, bool VARLEN, bool DQ_ATOMIC>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
-  constexpr int BM = kBwdBlockM;    // query rows per step
-  constexpr int BNK = kBwdBlockN;   // keys per workgroup
+__global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
+  constexpr int BM = kBwdBlockM;    // query rows per step (two 32-row halves)
+  constexpr int BNK = kBwdBlockN;   // keys per workgroup (four 32-key groups)
   constexpr int ROWB = D * 2;
   constexpr int QT_BYTES = BM * ROWB;
-  constexpr int STAGE = 2 * QT_BYTES + 2 * BM * 4;  // Q, dO, LSE*log2e, D
-  constexpr int KT_BYTES = DQ_ATOMIC ? BNK * ROWB : 0;
-  constexpr int DS_PITCH = BM * 2 + 8;              // bytes per key row of dS^T (padded)
-  constexpr int DS_BYTES = DQ_ATOMIC ? BNK * DS_PITCH : 0;
+  constexpr int STAGE = 2 * QT_BYTES + 2 * BM * 4;  // Q, dO, LSE*log2e, scale*D
+  constexpr int KT_BYTES = BNK * ROWB;
+  constexpr int DS_ROWB = BM * 2;                   // one key row of dS^T
+  constexpr int DS_BYTES = DQ_ATOMIC ? BNK * DS_ROWB : 0;
   constexpr int SLOTS = D / 8, NDS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE + KT_BYTES + 2 * DS_BYTES];
+  constexpr int MAIN_BYTES = STAGE + 2 * KT_BYTES + 2 * DS_BYTES;
+  constexpr int RED_BYTES = 4 * 64 * (2 * D / 2) * 4;  // 4 waves x 64 lanes x (dK,dV halves) fp32
+  constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  FA_LDS char* k_lds = smem + 2 * STAGE;
-  FA_LDS char* dsh_lds = k_lds + KT_BYTES;
+  FA_LDS char* qt = smem;
+  FA_LDS char* dot = qt + QT_BYTES;
+  FA_LDS float* lse_l = (FA_LDS float*)(dot + QT_BYTES);
+  FA_LDS float* dvec_l = lse_l + BM;
+  FA_LDS char* k_lds = smem + STAGE;
+  FA_LDS char* v_lds = k_lds + KT_BYTES;
+  FA_LDS char* dsh_lds = v_lds + KT_BYTES;
   FA_LDS char* dsl_lds = dsh_lds + DS_BYTES;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = wave & 3;   // key group
+  const int qh = wave >> 2;  // row half of each step
   const int hl = lane >> 5;
   const int i16 = lane & 15;
 
@@ -207,22 +241,16 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + sq.dooff, rows_bytes(Lq, p.do_ss, ROWB));
   const rsrc_t rk = make_rsrc((const uint16_t*)p.k + sq.koff, rows_bytes(Lk, p.k_ss, ROWB));
   const rsrc_t rv = make_rsrc((const uint16_t*)p.v + sq.voff, rows_bytes(Lk, p.v_ss, ROWB));
+  const rsrc_t racc = make_rsrc(p.dq_acc + (DQ_ATOMIC ? sq.rowbase * D : 0), DQ_ATOMIC ? (uint32_t)Lq * D * 4 : 0u);
 
-  const int my_key = k_blk0 + 32 * wave + (lane & 31);
-  u32x4 kreg[NDS], vreg[NDS];
+  // K and V tiles of the block (rows past the end read as zero)
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    kreg[ds] = buf_load16(rk, (uint32_t)my_key * k_ss2 + (2 * ds + hl) * 16);
-    vreg[ds] = buf_load16(rv, (uint32_t)my_key * v_ss2 + (2 * ds + hl) * 16);
-  }
-  if constexpr (DQ_ATOMIC) {
-#pragma unroll
-    for (int i = wave; i < KT_BYTES / 1024; i += 4) {
-      const int idx = i * 64 + lane;
-      const int r = idx / SLOTS;
-      const int c = (idx % SLOTS) ^ slot_swizzle<D>(r);
-      buf_load_lds16(rk, k_lds + i * 1024, (uint32_t)(k_blk0 + r) * k_ss2 + c * 16);
-    }
+  for (int i = wave; i < KT_BYTES / 1024; i += 8) {
+    const int idx = i * 64 + lane;
+    const int r = idx / SLOTS;
+    const int cc = (idx % SLOTS) ^ slot_swizzle<D>(r);
+    buf_load_lds16(rk, k_lds + i * 1024, (uint32_t)(k_blk0 + r) * k_ss2 + cc * 16);
+    buf_load_lds16(rv, v_lds + i * 1024, (uint32_t)(k_blk0 + r) * v_ss2 + cc * 16);
   }
 
   const int i_start = CAUSAL ? k_blk0 / BM : 0;
@@ -230,17 +258,14 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int n_steps = i_end > i_start ? i_end - i_start : 0;
   const float c = p.scale_log2;
 
-  // Q/dO stage loader (DMA) and row terms (registers of threads 0..63)
-  auto issue_q = [&](int i, int stage) {
-    FA_LDS char* qd = smem + stage * STAGE;
-    FA_LDS char* dod = qd + QT_BYTES;
+  auto issue_q = [&](int i) {
 #pragma unroll
-    for (int j = wave; j < QT_BYTES / 1024; j += 4) {
+    for (int j = wave; j < QT_BYTES / 1024; j += 8) {
       const int idx = j * 64 + lane;
       const int r = idx / SLOTS;
       const int cc = (idx % SLOTS) ^ slot_swizzle<D>(r);
-      buf_load_lds16(rq, qd + j * 1024, (uint32_t)(i * BM + r) * q_ss2 + cc * 16);
-      buf_load_lds16(rdo, dod + j * 1024, (uint32_t)(i * BM + r) * do_ss2 + cc * 16);
+      buf_load_lds16(rq, qt + j * 1024, (uint32_t)(i * BM + r) * q_ss2 + cc * 16);
+      buf_load_lds16(rdo, dot + j * 1024, (uint32_t)(i * BM + r) * do_ss2 + cc * 16);
     }
   };
   float lse_next = 0.0f, dvec_next = 0.0f;
@@ -257,12 +282,18 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     }
   };
 
-  // lane-constant operand address parts (see fa_device.h for the layouts)
+  // lane-constant operand address parts
+  const int my_key = k_blk0 + 32 * kw + (lane & 31);
   const int sw_row = slot_swizzle<D>(lane & 15);
+  const int arow = (32 * qh + (lane & 31)) * ROWB;   // Q/dO row of the A operand
+  const int brow = (32 * kw + (lane & 31)) * ROWB;   // K/V row of the B operand
   const int tr_r1 = 4 * hl + (i16 >> 2);
   const int sw_t1 = slot_swizzle<D>(tr_r1), sw_t2 = slot_swizzle<D>(tr_r1 + 8);
   const int tr_clo = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
   const int tr_half = (i16 & 1) * 8;
+  const int krow = 32 * kw + (lane & 31);                  // this lane's key row of dS^T
+  const int ds_sw_w = ds_swizzle(krow);
+  const int ds_gcol = 4 * ((lane >> 4) & 1) + (i16 & 3);   // granule within a 32-query block
 
   f32x16 dvacc[NDB], dkacc[NDB];
 #pragma unroll
@@ -272,169 +303,182 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   }
 
   if (n_steps > 0) {
-    issue_q(i_start, 0);
+    issue_q(i_start);
     load_terms(i_start);
   }
   for (int it = 0; it < n_steps; ++it) {
     const int i = i_start + it;
-    const int stage = it & 1;
     const int q0 = i * BM;
-    FA_LDS char* qt = smem + stage * STAGE;
-    FA_LDS char* dot = qt + QT_BYTES;
-    FA_LDS float* lse_l = (FA_LDS float*)(dot + QT_BYTES);
-    FA_LDS float* dvec_l = lse_l + BM;
-    wait_vmem();
+    // wait for this stage's loads; the previous step's 16 dQ atomics (issued after
+    // them) may still be in flight
+    if (DQ_ATOMIC && it > 0 && kw < NDB) wait_vmem_keep16();
+    else wait_vmem();
     if (threadIdx.x < BM) {
       lse_l[threadIdx.x] = (lse_next == -INFINITY) ? INFINITY : lse_next * kLog2e;
-      dvec_l[threadIdx.x] = dvec_next;
+      dvec_l[threadIdx.x] = dvec_next * p.scale;
     }
     __syncthreads();
-    if (it + 1 < n_steps) {
-      issue_q(i + 1, stage ^ 1);
-      load_terms(i + 1);
-    }
 
-    // S = Q K^T (lane: key my_key; rows: queries q0 + 32qb + 8(r/4) + 4hl + (r&3))
-    f32x16 s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int coff = ((2 * ds + hl) ^ sw_row) << 4;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const u32x4 a = lds_read16(qt + (32 * qb + (lane & 31)) * ROWB + coff);
-        s[qb] = mfma_bf16(a, kreg[ds], s[qb]);
-        const u32x4 ad = lds_read16(dot + (32 * qb + (lane & 31)) * ROWB + coff);
-        dp[qb] = mfma_bf16(ad, vreg[ds], dp[qb]);
-      }
-    }
-
-    // P = 2^(s*c - LSE*log2 e), masked; dS = P (dP - D)
+    const int row0 = q0 + 32 * qh;   // first row of this wave's half
+    // every key of the wave after every row of its half: nothing visible
+    const bool skip = CAUSAL && (k_blk0 + 32 * kw > row0 + 31);
     bool need_mask = (k_blk0 + BNK > Lk);
-    if constexpr (CAUSAL) need_mask = need_mask || (q0 < k_blk0 + BNK);
-    u32x4 pb[4], dsh[4], dsl[4];
+    if constexpr (CAUSAL) need_mask = need_mask || (k_blk0 + 32 * kw + 31 > row0);
+    u32x4 dsh[2], dsl[2];
+    if (!skip) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l2 = *(const FA_LDS f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * hl);
-        const f32x4 dd = *(const FA_LDS f32x4*)(dvec_l + 32 * qb + 8 * r4 + 4 * hl);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * r4 + j;
-          float pe = exp2_hw(__builtin_fmaf(s[qb][r], c, -l2[j]));
-          if (need_mask) {
-            const int query = q0 + 32 * qb + 8 * r4 + 4 * hl + j;
-            bool hide = my_key >= Lk;
-            if constexpr (CAUSAL) hide = hide || my_key > query;
-            if (hide) pe = 0.0f;
-          }
-          pv[r] = pe;
-          dsv[r] = pe * (dp[qb][r] - dd[j]);
-        }
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int co = ((2 * ds + hl) ^ sw_row) << 4;
+        s = mfma_bf16(lds_read16(qt + arow + co), lds_read16(k_lds + brow + co), s);
+        dp = mfma_bf16(lds_read16(dot + arow + co), lds_read16(v_lds + brow + co), dp);
       }
+      u32x4 pb[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int g = 2 * qb + half;
         uint32_t ph[4], hh[4], ll[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a0 = dsv[8 * half + 2 * e], a1 = dsv[8 * half + 2 * e + 1];
-          ph[e] = pack_bf16(pv[8 * half + 2 * e], pv[8 * half + 2 * e + 1]);
-          hh[e] = pack_bf16(a0, a1);
-          ll[e] = pack_bf16(a0 - bf16_lo(hh[e]), a1 - bf16_hi(hh[e]));
+        for (int r4h = 0; r4h < 2; ++r4h) {
+          const int r4 = 2 * half + r4h;
+          const f32x4 l2 = *(const FA_LDS f32x4*)(lse_l + 32 * qh + 8 * r4 + 4 * hl);
+          const f32x4 dd = *(const FA_LDS f32x4*)(dvec_l + 32 * qh + 8 * r4 + 4 * hl);
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float pe = exp2_hw(__builtin_fmaf(s[4 * r4 + j], c, -l2[j]));
+            if (need_mask) {
+              const int query = row0 + 8 * r4 + 4 * hl + j;
+              bool hide = my_key >= Lk;
+              if constexpr (CAUSAL) hide = hide || my_key > query;
+              pe = hide ? 0.0f : pe;
+            }
+            pv[j] = pe;
+            dsv[j] = pe * __builtin_fmaf(dp[4 * r4 + j], p.scale, -dd[j]);  // scale * P (dP - D)
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int k = 2 * r4h + e;
+            ph[k] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+            hh[k] = pack_bf16(dsv[2 * e], dsv[2 * e + 1]);
+            ll[k] = pack_bf16(dsv[2 * e] - bf16_lo(hh[k]), dsv[2 * e + 1] - bf16_hi(hh[k]));
+          }
         }
-        pb[g] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-        dsh[g] = u32x4{hh[0], hh[1], hh[2], hh[3]};
-        dsl[g] = u32x4{ll[0], ll[1], ll[2], ll[3]};
+        pb[half] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        dsh[half] = u32x4{hh[0], hh[1], hh[2], hh[3]};
+        dsl[half] = u32x4{ll[0], ll[1], ll[2], ll[3]};
       }
-    }
-
-    // dV^T += dO^T P ; dK^T += Q^T dS  (A operands through the transpose reads)
+      // dV^T += dO^T P ; dK^T += Q^T dS'  (16-row groups of this half)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r1 = 16 * g + tr_r1;
+      for (int half = 0; half < 2; ++half) {
+        const int r1 = 32 * qh + 16 * half + tr_r1;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int cc = 4 * db + tr_clo;
-        const int o1 = r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half;
-        const int o2 = (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half;
-        const u32x2 a_lo = lds_read_tr16(dot + o1), a_hi = lds_read_tr16(dot + o2);
-        dvacc[db] = mfma_bf16(u32x4{a_lo[0], a_lo[1], a_hi[0], a_hi[1]}, pb[g], dvacc[db]);
-        const u32x2 q_lo = lds_read_tr16(qt + o1), q_hi = lds_read_tr16(qt + o2);
-        const u32x4 qa = u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]};
-        dkacc[db] = mfma_bf16(qa, dsh[g], dkacc[db]);
-        dkacc[db] = mfma_bf16(qa, dsl[g], dkacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const int cc = 4 * db + tr_clo;
+          const int o1 = r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half;
+          const int o2 = (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half;
+          const u32x2 a_lo = lds_read_tr16(dot + o1), a_hi = lds_read_tr16(dot + o2);
+          dvacc[db] = mfma_bf16(u32x4{a_lo[0], a_lo[1], a_hi[0], a_hi[1]}, pb[half], dvacc[db]);
+          const u32x2 q_lo = lds_read_tr16(qt + o1), q_hi = lds_read_tr16(qt + o2);
+          const u32x4 qa = u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]};
+          dkacc[db] = mfma_bf16(qa, dsh[half], dkacc[db]);
+          dkacc[db] = mfma_bf16(qa, dsl[half], dkacc[db]);
+        }
       }
+    } else {
+      dsh[0] = dsh[1] = dsl[0] = dsl[1] = u32x4{0u, 0u, 0u, 0u};
     }
-
     if constexpr (DQ_ATOMIC) {
-      // dS^T rows (keys) to LDS: 4 consecutive queries per 8-byte write
-      const int krow = 32 * wave + (lane & 31);
+      // dS'^T to LDS: granule (8qh + 2r4 + hl) of row krow holds rows 32qh + 8r4 + 4hl + 0..3
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int g = 2 * qb + (r4 >> 1);
-          const int e = 2 * (r4 & 1);
-          const int off = krow * DS_PITCH + (32 * qb + 8 * r4 + 4 * hl) * 2;
-          *(FA_LDS u32x2*)(dsh_lds + off) = u32x2{dsh[g][e], dsh[g][e + 1]};
-          *(FA_LDS u32x2*)(dsl_lds + off) = u32x2{dsl[g][e], dsl[g][e + 1]};
-        }
-      __syncthreads();
-      // dQ (64 x D) = dS (64 x 128) K (128 x D): blocks (qb, db) spread over the 4 waves
-      for (int blk = wave; blk < 2 * NDB; blk += 4) {
-        const int qb = blk / NDB, db = blk - qb * NDB;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int half = r4 >> 1, e = 2 * (r4 & 1);
+        const int off = krow * DS_ROWB + (((8 * qh + 2 * r4 + hl) ^ ds_sw_w) << 3);
+        *(FA_LDS u32x2*)(dsh_lds + off) = u32x2{dsh[half][e], dsh[half][e + 1]};
+        *(FA_LDS u32x2*)(dsl_lds + off) = u32x2{dsl[half][e], dsl[half][e + 1]};
+      }
+    }
+    __syncthreads();  // stage consumed by every wave (and dS' complete)
+    if (it + 1 < n_steps) {
+      issue_q(i + 1);
+      load_terms(i + 1);
+    }
+    if constexpr (DQ_ATOMIC) {
+      // this wave's dQ block: rows q0 + 32qh + ..., columns 32kw + (lane & 31)
+      if (kw < NDB) {
         f32x16 acc = f32x16{};
-        const int dcol = (32 * qb + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3)) * 2;
-        const int cc = 4 * db + tr_clo;
+        const int cc = 4 * kw + tr_clo;
 #pragma unroll
         for (int g = 0; g < BNK / 16; ++g) {
           const int r1 = 16 * g + tr_r1;
-          const u32x2 h1 = lds_read_tr16(dsh_lds + r1 * DS_PITCH + dcol);
-          const u32x2 h2 = lds_read_tr16(dsh_lds + (r1 + 8) * DS_PITCH + dcol);
-          const u32x2 l1 = lds_read_tr16(dsl_lds + r1 * DS_PITCH + dcol);
-          const u32x2 l2 = lds_read_tr16(dsl_lds + (r1 + 8) * DS_PITCH + dcol);
           const u32x2 k1 = lds_read_tr16(k_lds + r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half);
           const u32x2 k2 = lds_read_tr16(k_lds + (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half);
           const u32x4 kb = u32x4{k1[0], k1[1], k2[0], k2[1]};
+          const int c8 = 8 * qh + ds_gcol;
+          const int oa = r1 * DS_ROWB + ((c8 ^ ds_swizzle(r1)) << 3);
+          const int ob = (r1 + 8) * DS_ROWB + ((c8 ^ ds_swizzle(r1 + 8)) << 3);
+          const u32x2 h1 = lds_read_tr16(dsh_lds + oa), h2 = lds_read_tr16(dsh_lds + ob);
+          const u32x2 l1 = lds_read_tr16(dsl_lds + oa), l2 = lds_read_tr16(dsl_lds + ob);
           acc = mfma_bf16(u32x4{h1[0], h1[1], h2[0], h2[1]}, kb, acc);
           acc = mfma_bf16(u32x4{l1[0], l1[1], l2[0], l2[1]}, kb, acc);
         }
-        const int d = 32 * db + (lane & 31);
+        const uint32_t rowb = (uint32_t)(row0 + 4 * hl) * (D * 4) + (uint32_t)(32 * kw + (lane & 31)) * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = q0 + 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (query < Lq) atomicAdd(p.dq_acc + (sq.rowbase + query) * D + d, acc[r] * p.scale);
-        }
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], racc, rowb + (uint32_t)(8 * (r >> 2) + (r & 3)) * (D * 4),
+                                                          0, 0);
       }
     }
   }
 
-  // ---- write dK = scale * dK^T acc, dV ----
-  const int gb = p.grad_bf16 ? 2 : 4;
-  const rsrc_t rdk = make_rsrc((char*)p.dk + sq.dkoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dk_ss * gb) + D * gb : 0u);
-  const rsrc_t rdv = make_rsrc((char*)p.dv + sq.dvoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dv_ss * gb) + D * gb : 0u);
-  const uint32_t dk_row = (uint32_t)my_key * (uint32_t)(p.dk_ss * gb);
-  const uint32_t dv_row = (uint32_t)my_key * (uint32_t)(p.dv_ss * gb);
+  // ---- sum the two row-half partials of each key group, then store dK, dV ----
+  __syncthreads();
+  FA_LDS f32x4* red = (FA_LDS f32x4*)smem + kw * (64 * 2 * NDB * 4);
+  if (qh == 1) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * db + 8 * r4 + 4 * hl;
-      store_grad4(rdk, dk_row + d * 4, dk_row + d * 2, p.grad_bf16, dkacc[db][4 * r4] * p.scale,
-                  dkacc[db][4 * r4 + 1] * p.scale, dkacc[db][4 * r4 + 2] * p.scale, dkacc[db][4 * r4 + 3] * p.scale);
-      store_grad4(rdv, dv_row + d * 4, dv_row + d * 2, p.grad_bf16, dvacc[db][4 * r4], dvacc[db][4 * r4 + 1],
-                  dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]);
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        red[((2 * db) * 4 + r4) * 64 + lane] = f32x4{dkacc[db][4 * r4], dkacc[db][4 * r4 + 1], dkacc[db][4 * r4 + 2], dkacc[db][4 * r4 + 3]};
+        red[((2 * db + 1) * 4 + r4) * 64 + lane] = f32x4{dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    const int gb = p.grad_bf16 ? 2 : 4;
+    const rsrc_t rdk = make_rsrc((char*)p.dk + sq.dkoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dk_ss * gb) + D * gb : 0u);
+    const rsrc_t rdv = make_rsrc((char*)p.dv + sq.dvoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dv_ss * gb) + D * gb : 0u);
+    const uint32_t dk_row = (uint32_t)my_key * (uint32_t)(p.dk_ss * gb);
+    const uint32_t dv_row = (uint32_t)my_key * (uint32_t)(p.dv_ss * gb);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * hl;
+        const f32x4 ok = red[((2 * db) * 4 + r4) * 64 + lane];
+        const f32x4 ov = red[((2 * db + 1) * 4 + r4) * 64 + lane];
+        store_grad4(rdk, dk_row + d * 4, dk_row + d * 2, p.grad_bf16, dkacc[db][4 * r4] + ok[0],
+                    dkacc[db][4 * r4 + 1] + ok[1], dkacc[db][4 * r4 + 2] + ok[2], dkacc[db][4 * r4 + 3] + ok[3]);
+        store_grad4(rdv, dv_row + d * 4, dv_row + d * 2, p.grad_bf16, dvacc[db][4 * r4] + ov[0],
+                    dvacc[db][4 * r4 + 1] + ov[1], dvacc[db][4 * r4 + 2] + ov[2], dvacc[db][4 * r4 + 3] + ov[3]);
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dq (deterministic mode): dQ for 128 query rows, no atomics.
+// bwd_dq (deterministic mode): dQ for 256 query rows, no atomics.
+//
+// Shaped like the forward: eight waves (two per SIMD) of 32 rows each keep Q and
+// dO in registers as B operands; K and V tiles of 64 keys stream through a
+// double-buffered LDS stage.  Per tile and 32-key block:
+//   S^T = K Q^T, dP^T = V dO^T      (lane = query row, registers = keys)
+//   dS'^T = scale * P^T (dP^T - D)  with P^T = 2^(S^T*c - LSE*log2 e)
+//   dQ^T += K^T [dS'_hi; dS'_lo]    (A = K^T by transpose reads)
+// dQ is reduced in registers in a fixed order and written once.
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int BN = kFwdBlockN;
+  constexpr int NW = 8;
+  constexpr int WG_ROWS = 32 * NW;
   constexpr int ROWB = D * 2;
   constexpr int TILE_BYTES = BN * ROWB;
   constexpr int STAGE_BYTES = 2 * TILE_BYTES;
@@ -458,14 +502,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const int bh_count = p.batch * p.heads;
     const int t = blockIdx.x / bh_count;
     const int bh = blockIdx.x - t * bh_count;
-    const int n_qt = (p.seqlen_q + kFwdTileRows - 1) / kFwdTileRows;
+    const int n_qt = (p.seqlen_q + WG_ROWS - 1) / WG_ROWS;
     qtile = CAUSAL ? (n_qt - 1 - t) : t;
     b = bh / p.heads;
     h = bh - b * p.heads;
   }
   const BwdSeq sq = bwd_seq(p, b, h);
   const int Lq = sq.Lq, Lk = sq.Lk;
-  const int wg_q0 = qtile * kFwdTileRows;
+  const int wg_q0 = qtile * WG_ROWS;
   if (wg_q0 >= Lq) return;
 
   const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), do_ss2 = (uint32_t)(p.do_ss * 2);
@@ -475,7 +519,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const rsrc_t rk = make_rsrc((const uint16_t*)p.k + sq.koff, rows_bytes(Lk, p.k_ss, ROWB));
   const rsrc_t rv = make_rsrc((const uint16_t*)p.v + sq.voff, rows_bytes(Lk, p.v_ss, ROWB));
 
-  const int q0 = wg_q0 + wave * 32;
+  // rows of this wave: two 128-row tiles interleaved so that the two waves of a
+  // SIMD hold neighbouring row blocks
+  const int q0 = wg_q0 + 32 * wave;
   const int my_row = q0 + (lane & 31);
   u32x4 qreg[NDS], doreg[NDS];
 #pragma unroll
@@ -483,23 +529,25 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     qreg[ds] = buf_load16(rq, (uint32_t)my_row * q_ss2 + (2 * ds + hl) * 16);
     doreg[ds] = buf_load16(rdo, (uint32_t)my_row * do_ss2 + (2 * ds + hl) * 16);
   }
-  float lse2 = INFINITY, dvec = 0.0f;
+  float lse2 = INFINITY, dvs = 0.0f;
   if (my_row < Lq) {
     const float l = p.lse[sq.lseoff + my_row];
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    dvec = p.dvec[sq.rowbase + my_row];
+    dvs = p.dvec[sq.rowbase + my_row] * p.scale;
   }
 
   int kv_end = Lk;
-  if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + kFwdTileRows));
+  if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + WG_ROWS));
   const int n_tiles = (kv_end + BN - 1) / BN;
+  int n_mine = n_tiles;
+  if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 31) / BN + 1);
 
   auto issue_tile = [&](int t, int stage) {
     const int k0 = t * BN;
     FA_LDS char* kd = smem + stage * STAGE_BYTES;
     FA_LDS char* vd = kd + TILE_BYTES;
 #pragma unroll
-    for (int i = wave; i < TILE_BYTES / 1024; i += 4) {
+    for (int i = wave; i < TILE_BYTES / 1024; i += NW) {
       const int idx = i * 64 + lane;
       const int r = idx / SLOTS;
       const int cc = (idx % SLOTS) ^ slot_swizzle<D>(r);
@@ -520,74 +568,71 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
   if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
+  int t = 0;
+  for (; t < n_mine; ++t) {
     const int stage = t & 1;
     wait_vmem();
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
     const int k0 = t * BN;
-    if (CAUSAL && k0 > q0 + 31) continue;
     const FA_LDS char* kt = smem + stage * STAGE_BYTES;
     const FA_LDS char* vt = kt + TILE_BYTES;
-
-    // S^T = K Q^T and dP^T = V dO^T (lane: query my_row; regs: keys)
-    f32x16 s[NKB], dp[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = dp[kb] = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int coff = ((2 * ds + hl) ^ sw_row) << 4;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int ro = (32 * kb + (lane & 31)) * ROWB + coff;
-        s[kb] = mfma_bf16(lds_read16(kt + ro), qreg[ds], s[kb]);
-        dp[kb] = mfma_bf16(lds_read16(vt + ro), doreg[ds], dp[kb]);
-      }
-    }
     bool need_mask = (k0 + BN > Lk);
     if constexpr (CAUSAL) need_mask = need_mask || (k0 + BN - 1 > q0);
-    u32x4 dsh[2 * NKB], dsl[2 * NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      float dsv[16];
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pe = exp2_hw(__builtin_fmaf(s[kb][r], c, -lse2));
-        if (need_mask) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          bool hide = key >= Lk;
-          if constexpr (CAUSAL) hide = hide || key > my_row;
-          if (hide) pe = 0.0f;
-        }
-        dsv[r] = pe * (dp[kb][r] - dvec);
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int ro = (32 * kb + (lane & 31)) * ROWB + (((2 * ds + hl) ^ sw_row) << 4);
+        s = mfma_bf16(lds_read16(kt + ro), qreg[ds], s);
+        dp = mfma_bf16(lds_read16(vt + ro), doreg[ds], dp);
       }
+      u32x4 dsh[2], dsl[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         uint32_t hh[4], ll[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a0 = dsv[8 * half + 2 * e], a1 = dsv[8 * half + 2 * e + 1];
-          hh[e] = pack_bf16(a0, a1);
-          ll[e] = pack_bf16(a0 - bf16_lo(hh[e]), a1 - bf16_hi(hh[e]));
+          float dv2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 8 * half + 2 * e + u;
+            float pe = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
+            if (need_mask) {
+              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+              bool hide = key >= Lk;
+              if constexpr (CAUSAL) hide = hide || key > my_row;
+              pe = hide ? 0.0f : pe;
+            }
+            dv2[u] = pe * __builtin_fmaf(dp[r], p.scale, -dvs);   // scale * P (dP - D)
+          }
+          hh[e] = pack_bf16(dv2[0], dv2[1]);
+          ll[e] = pack_bf16(dv2[0] - bf16_lo(hh[e]), dv2[1] - bf16_hi(hh[e]));
         }
-        dsh[2 * kb + half] = u32x4{hh[0], hh[1], hh[2], hh[3]};
-        dsl[2 * kb + half] = u32x4{ll[0], ll[1], ll[2], ll[3]};
+        dsh[half] = u32x4{hh[0], hh[1], hh[2], hh[3]};
+        dsl[half] = u32x4{ll[0], ll[1], ll[2], ll[3]};
+      }
+      // dQ^T += K^T dS'^T  (A = K^T through the transpose reads, 16-key groups)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int r1 = 32 * kb + 16 * half + tr_r1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int cc = 4 * db + tr_clo;
+          const u32x2 lo = lds_read_tr16(kt + r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half);
+          const u32x2 hi = lds_read_tr16(kt + (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half);
+          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          dqacc[db] = mfma_bf16(a, dsh[half], dqacc[db]);
+          dqacc[db] = mfma_bf16(a, dsl[half], dqacc[db]);
+        }
       }
     }
-    // dQ^T += K^T dS^T (A = K^T through the transpose reads)
-#pragma unroll
-    for (int g = 0; g < BN / 16; ++g) {
-      const int r1 = 16 * g + tr_r1;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int cc = 4 * db + tr_clo;
-        const u32x2 lo = lds_read_tr16(kt + r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half);
-        const u32x2 hi = lds_read_tr16(kt + (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half);
-        const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        dqacc[db] = mfma_bf16(a, dsh[g], dqacc[db]);
-        dqacc[db] = mfma_bf16(a, dsl[g], dqacc[db]);
-      }
-    }
+  }
+  for (; t < n_tiles; ++t) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, (t & 1) ^ 1);
   }
 
   const int gb = p.grad_bf16 ? 2 : 4;
@@ -598,8 +643,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = 32 * db + 8 * r4 + 4 * hl;
-      store_grad4(rdq, row_off + d * 4, row_off + d * 2, p.grad_bf16, dqacc[db][4 * r4] * p.scale,
-                  dqacc[db][4 * r4 + 1] * p.scale, dqacc[db][4 * r4 + 2] * p.scale, dqacc[db][4 * r4 + 3] * p.scale);
+      store_grad4(rdq, row_off + d * 4, row_off + d * 2, p.grad_bf16, dqacc[db][4 * r4], dqacc[db][4 * r4 + 1],
+                  dqacc[db][4 * r4 + 2], dqacc[db][4 * r4 + 3]);
     }
 }
 
@@ -673,7 +718,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t strea
       grid = (unsigned)((p.seqlen_k + kBwdBlockN - 1) / kBwdBlockN) * (unsigned)(p.batch * p.heads);
     }
     if (grid > 0) {
-#define FA_KV(C, V, A) hipLaunchKernelGGL((bwd_kv_kernel<D, C, V, A>), dim3(grid), dim3(256), 0, stream, p)
+#define FA_KV(C, V, A) hipLaunchKernelGGL((bwd_kv_kernel<D, C, V, A>), dim3(grid), dim3(512), 0, stream, p)
       if (p.causal) {
         if (p.varlen) { if (atomic) FA_KV(true, true, true); else FA_KV(true, true, false); }
         else { if (atomic) FA_KV(true, false, true); else FA_KV(true, false, false); }
@@ -699,16 +744,16 @@ static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t strea
   unsigned grid;
   int32_t* qsched = p.sched + 1 + 2 * ((p.total_k + kBwdBlockN - 1) / kBwdBlockN + p.batch);
   if (p.varlen) {
-    hipError_t e = launch_fwd_schedule(p.cu_q, p.cu_k, p.batch, kFwdTileRows, kFwdBlockN, p.causal, qsched, stream);
+    hipError_t e = launch_fwd_schedule(p.cu_q, p.cu_k, p.batch, kDqTileRows, kFwdBlockN, p.causal, qsched, stream);
     if (e != hipSuccess) return e;
-    grid = (unsigned)((p.total_q + kFwdTileRows - 1) / kFwdTileRows + p.batch) * (unsigned)p.heads;
+    grid = (unsigned)((p.total_q + kDqTileRows - 1) / kDqTileRows + p.batch) * (unsigned)p.heads;
   } else {
-    grid = (unsigned)((p.seqlen_q + kFwdTileRows - 1) / kFwdTileRows) * (unsigned)(p.batch * p.heads);
+    grid = (unsigned)((p.seqlen_q + kDqTileRows - 1) / kDqTileRows) * (unsigned)(p.batch * p.heads);
   }
   if (grid == 0) return hipSuccess;
   BwdParams pq = p;
   pq.sched = qsched;
-#define FA_DQ(C, V) hipLaunchKernelGGL((bwd_dq_kernel<D, C, V>), dim3(grid), dim3(256), 0, stream, pq)
+#define FA_DQ(C, V) hipLaunchKernelGGL((bwd_dq_kernel<D, C, V>), dim3(grid), dim3(512), 0, stream, pq)
   if (p.causal) { if (p.varlen) FA_DQ(true, true); else FA_DQ(true, false); }
   else { if (p.varlen) FA_DQ(false, true); else FA_DQ(false, false); }
 #undef FA_DQ

@@ -64,6 +64,11 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// s_waitcnt vmcnt(16): vector memory operations retire in issue order, so this
+// waits for everything but the 16 most recent ones (e.g. fire-and-forget atomics
+// issued after a stage's loads).
+__device__ __forceinline__ void wait_vmem_keep16() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+
 __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

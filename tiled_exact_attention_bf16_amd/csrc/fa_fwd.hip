@@ -135,14 +135,18 @@ __global__ __launch_bounds__(256 * NQT) void fwd_kernel(FwdParams p) {
   float lsum_r = 0.0f;  // sum of bf16-rounded weights
   const float c = p.scale_log2;
 
+  // Under the causal mask a wave's rows stop seeing keys before the workgroup's
+  // last tile; it then only helps stage K/V (second loop) and keeps the barriers.
+  int n_mine = n_tiles;
+  if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 31) / BN + 1);
   if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
+  int t = 0;
+  for (; t < n_mine; ++t) {
     const int stage = t & 1;
     wait_vmem();
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
     const int k0 = t * BN;
-    if (CAUSAL && k0 > q0 + 31) continue;  // every key of the tile is after every row of the wave
 
     const FA_LDS char* kt = smem + stage * STAGE_BYTES;
     const FA_LDS char* vt = kt + TILE_BYTES;
@@ -241,6 +245,11 @@ __global__ __launch_bounds__(256 * NQT) void fwd_kernel(FwdParams p) {
         oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
       }
     }
+  }
+  for (; t < n_tiles; ++t) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(t + 1, (t & 1) ^ 1);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l ----

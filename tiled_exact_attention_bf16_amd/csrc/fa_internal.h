@@ -11,6 +11,7 @@ constexpr int kFwdTileRows = 128;  // query rows per tile (4 waves x 32 rows)
 constexpr int kFwdBlockN = 64;     // keys per K/V stage in the forward
 constexpr int kBwdBlockN = 128;    // keys per backward work item (4 waves x 32 keys)
 constexpr int kBwdBlockM = 64;     // query rows per backward step
+constexpr int kDqTileRows = 256;   // query rows per dQ work item (deterministic mode)
 constexpr int kSchedMaxCost = 8192;  // histogram bins of the longest-first sort
 
 struct FwdParams {
