@@ -176,8 +176,10 @@ __device__ __forceinline__ void store_grad4(rsrc_t r, uint32_t byte_off_f32, uin
 // 32x32 block of dQ = dS' K and adds it with fp32 buffer atomics (rows past the end
 // are dropped by the buffer range check).
 //
-// The Q/dO stage is single-buffered: the next step's DMA is issued after the second
-// barrier (once every wave has finished reading the stage) and overlaps the dQ part.
+// The Q/dO stage is double-buffered in deterministic mode (the next step streams in
+// while the current one is used).  In atomic mode the dS' staging leaves room for a
+// single stage only: its refill is issued after the second barrier (once every wave
+// has finished reading it) and overlaps the dQ part.
 //
 // dS'^T LDS layout: [128 keys][64 queries] bf16, 128-byte rows of sixteen 8-byte
 // granules; granule g of row r is stored at g ^ ds_swizzle(r), which keeps both the
@@ -195,16 +197,15 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   constexpr int DS_ROWB = BM * 2;                   // one key row of dS^T
   constexpr int DS_BYTES = DQ_ATOMIC ? BNK * DS_ROWB : 0;
   constexpr int SLOTS = D / 8, NDS = D / 16, NDB = D / 32;
-  constexpr int MAIN_BYTES = STAGE + 2 * KT_BYTES + 2 * DS_BYTES;
+  // Deterministic mode needs no dS staging, which leaves room to double-buffer the
+  // Q/dO stage; the atomic mode's single stage is refilled during its dQ part.
+  constexpr int NSTAGE = DQ_ATOMIC ? 1 : 2;
+  constexpr int MAIN_BYTES = NSTAGE * STAGE + 2 * KT_BYTES + 2 * DS_BYTES;
   constexpr int RED_BYTES = 4 * 64 * (2 * D / 2) * 4;  // 4 waves x 64 lanes x (dK,dV halves) fp32
   constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  FA_LDS char* qt = smem;
-  FA_LDS char* dot = qt + QT_BYTES;
-  FA_LDS float* lse_l = (FA_LDS float*)(dot + QT_BYTES);
-  FA_LDS float* dvec_l = lse_l + BM;
-  FA_LDS char* k_lds = smem + STAGE;
+  FA_LDS char* k_lds = smem + NSTAGE * STAGE;
   FA_LDS char* v_lds = k_lds + KT_BYTES;
   FA_LDS char* dsh_lds = v_lds + KT_BYTES;
   FA_LDS char* dsl_lds = dsh_lds + DS_BYTES;
@@ -258,7 +259,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   const int n_steps = i_end > i_start ? i_end - i_start : 0;
   const float c = p.scale_log2;
 
-  auto issue_q = [&](int i) {
+  auto issue_q = [&](int i, int stage) {
+    FA_LDS char* qt = smem + stage * STAGE;
+    FA_LDS char* dot = qt + QT_BYTES;
 #pragma unroll
     for (int j = wave; j < QT_BYTES / 1024; j += 8) {
       const int idx = j * 64 + lane;
@@ -303,12 +306,17 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   }
 
   if (n_steps > 0) {
-    issue_q(i_start);
+    issue_q(i_start, 0);
     load_terms(i_start);
   }
   for (int it = 0; it < n_steps; ++it) {
     const int i = i_start + it;
     const int q0 = i * BM;
+    const int stage = NSTAGE == 2 ? (it & 1) : 0;
+    FA_LDS char* qt = smem + stage * STAGE;
+    FA_LDS char* dot = qt + QT_BYTES;
+    FA_LDS float* lse_l = (FA_LDS float*)(dot + QT_BYTES);
+    FA_LDS float* dvec_l = lse_l + BM;
     // wait for this stage's loads; the previous step's 16 dQ atomics (issued after
     // them) may still be in flight
     if (DQ_ATOMIC && it > 0 && kw < NDB) wait_vmem_keep16();
@@ -318,6 +326,11 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
       dvec_l[threadIdx.x] = dvec_next * p.scale;
     }
     __syncthreads();
+    if (NSTAGE == 2 && it + 1 < n_steps) {
+      // the other stage was consumed in the previous step (before the barrier above)
+      issue_q(i + 1, stage ^ 1);
+      load_terms(i + 1);
+    }
 
     const int row0 = q0 + 32 * qh;   // first row of this wave's half
     // every key of the wave after every row of its half: nothing visible
@@ -397,12 +410,12 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
         *(FA_LDS u32x2*)(dsl_lds + off) = u32x2{dsl[half][e], dsl[half][e + 1]};
       }
     }
-    __syncthreads();  // stage consumed by every wave (and dS' complete)
-    if (it + 1 < n_steps) {
-      issue_q(i + 1);
-      load_terms(i + 1);
-    }
     if constexpr (DQ_ATOMIC) {
+      __syncthreads();  // stage consumed by every wave and dS' complete
+      if (it + 1 < n_steps) {
+        issue_q(i + 1, 0);
+        load_terms(i + 1);
+      }
       // this wave's dQ block: rows q0 + 32qh + ..., columns 32kw + (lane & 31)
       if (kw < NDB) {
         f32x16 acc = f32x16{};
