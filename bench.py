@@ -2,8 +2,8 @@
 """Throughput of exact tiled attention (BF16) on one MI355X.
 
 One step = the whole hot path on one batch: fa_fwd (O, LSE) then fa_bwd (dQ, dK,
-dV, atomic dQ) on the causal B=2, H=16, S=8192, d=128 workload (synthetic
-normal inputs, already resident in HBM).  Throughput counts algorithmic FLOP:
+dV; deterministic dQ by default, --atomic for atomic dQ) on the causal B=2, H=16,
+S=8192, d=128 workload (synthetic normal inputs, already resident in HBM).  Throughput counts algorithmic FLOP:
 4*d per visible (query, key) pair forward and 10*d backward, causal pairs only.
 
 Prints one JSON line.  Per-kernel average durations come from HIP events on the
@@ -68,7 +68,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--deterministic", action="store_true", help="time the deterministic backward")
+    ap.add_argument("--atomic", action="store_true",
+                    help="time the backward with atomic dQ accumulation (default: the deterministic mode)")
     ap.add_argument("--q-tiles", type=int, default=-1)
     ap.add_argument("--poly", type=int, default=-1)
     ap.add_argument("--tau", type=int, default=-1)
@@ -99,9 +100,9 @@ def main():
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")   # >= the backward's accumulator
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")   # >= either mode's workspace (fp32 dQ accumulator)
     tuning = FA.Tuning(args.poly, args.tau, args.q_tiles)
-    det = args.deterministic
+    det = not args.atomic
 
     def fwd():
         FA.fwd(q, k, v, inp.scale, True, tuning=tuning, out=o, lse=lse)
@@ -129,8 +130,7 @@ def main():
         e[2].record()
         bwd(L.FA_BWD_PHASE_MAIN)
         e[3].record()
-        if not det:
-            bwd(L.FA_BWD_PHASE_POST)
+        bwd(L.FA_BWD_PHASE_POST)
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -145,11 +145,17 @@ def main():
     bwd_ms = per["bwd_pre"] + per["bwd_main"] + per["bwd_post"]
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
-    dominant = max(("fwd", "bwd_main"), key=lambda n: per[n])
-    dom_flop = f_fwd if dominant == "fwd" else f_bwd
-    achieved = dom_flop / (per[dominant] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fa::fwd_kernel<128,2,causal>", "bwd_main": "fa::bwd_kv_kernel<128,causal,atomic>"
-                    if not det else "fa::bwd_kv_kernel + fa::bwd_dq_kernel"}
+    # algorithmic FLOP per visible pair for each kernel: forward 4d (S, PV); key-block
+    # kernel 8d (S, dP, dV, dK) in deterministic mode, 10d with the atomic dQ product;
+    # deterministic dQ kernel 2d (dQ; its S and dP are recomputation)
+    pairs = W.total_pairs(seq, seq, H, True)
+    alg = {"fwd": 4 * D * pairs, "bwd_main": (8 if det else 10) * D * pairs,
+           "bwd_post": 2 * D * pairs if det else 0, "bwd_pre": 0}
+    dominant = max(("fwd", "bwd_main", "bwd_post"), key=lambda n: per[n])
+    achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fa::fwd_kernel<128,2,causal>",
+                    "bwd_main": "fa::bwd_kv_kernel<128,causal," + ("deterministic>" if det else "atomic>"),
+                    "bwd_post": "fa::bwd_dq_kernel<128,causal>" if det else "fa::bwd_post_kernel<128>"}
     out = {
         "metric": "attention fwd/bwd TFLOP/s (BF16, d=128, causal S=8K) and % of MFMA peak",
         "value": round(value, 2),

@@ -171,9 +171,11 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, 
 /* The backward's three phases, enqueued in this order by fa_bwd:
  *   FA_BWD_PHASE_PRE:  row terms D_i = sum_d dO_id O_id into the workspace (and, in
  *                      atomic mode, zeroing of the fp32 dQ accumulator);
- *   FA_BWD_PHASE_MAIN: the gradient products (dK, dV; dQ by atomics into the
- *                      accumulator, or directly in deterministic mode);
- *   FA_BWD_PHASE_POST: atomic mode only: dQ from the accumulator in dQ's layout/dtype.
+ *   FA_BWD_PHASE_MAIN: the key-block kernel: dK and dV (and, in atomic mode, dQ
+ *                      added by fp32 atomics into the accumulator);
+ *   FA_BWD_PHASE_POST: dQ in dQ's layout and dtype: atomic mode converts the
+ *                      accumulator; deterministic mode runs the query-block kernel
+ *                      that reduces dQ in a fixed order.
  * fa_bwd_phases runs the selected subset (a bitwise OR) on the same arguments and
  * workspace, so callers can time or interleave them; a phase reads what the earlier
  * phases left in the workspace, so running MAIN without a preceding PRE on that

@@ -744,8 +744,8 @@ static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t strea
       if (e != hipSuccess) return e;
     }
   }
+  if (!(phases & 4)) return hipSuccess;
   if (atomic) {
-    if (!(phases & 4)) return hipSuccess;
     int64_t work = rows * (D / 4);
     int grid = (int)std::min<int64_t>((work + 255) / 256, 2048 * 4);
     if (grid < 1) grid = 1;
@@ -753,7 +753,6 @@ static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t strea
     return hipGetLastError();
   }
   // deterministic: query-major dQ kernel; its list reuses the forward's query-tile order
-  if (!(phases & 2)) return hipSuccess;
   unsigned grid;
   int32_t* qsched = p.sched + 1 + 2 * ((p.total_k + kBwdBlockN - 1) / kBwdBlockN + p.batch);
   if (p.varlen) {
