@@ -155,12 +155,18 @@ def test_rescale_threshold_zero_and_eight_agree():
     o8, l8 = FA.fwd(q, k, v, inp.scale, True, tuning=FA.Tuning(0, 8, 2))
     o0, l0 = FA.fwd(q, k, v, inp.scale, True, tuning=FA.Tuning(0, 0, 2))
     torch.cuda.synchronize()
-    # both are checked against the oracle elsewhere; between themselves they may
-    # differ by the rounding of the bf16 output (one unit in its last place)
+    # Both are checked against the oracle elsewhere.  Between themselves they differ
+    # by how the unnormalised weights round to bf16 under the two references: each
+    # weight carries a relative error of at most 2^-9 either way, which moves the
+    # normalised average by at most 2 * 2^-9 * max_j |v_j - o|; then the bf16
+    # rounding of the output itself (up to two units in its last place).
     a8, a0 = o8.float(), o0.float()
+    vmax = v.float().abs().amax(dim=(1, 3), keepdim=True)        # per (batch, head)
     ulp = torch.exp2(torch.floor(torch.log2(torch.maximum(a8.abs(), a0.abs()).clamp_min(2 ** -126))) - 7)
-    excess = ((a8 - a0).abs() - ulp).max().item()
+    bound = 2 * ulp + 2.0 ** -8 * (vmax + a0.abs())
+    excess = ((a8 - a0).abs() - bound).max().item()
     d = (a8 - a0).abs().max().item()
     dl = (l8 - l0).abs().max().item()
-    say(f"[lazy vs eager] O max diff {d:.3e} (max excess over one bf16 ulp {excess:.3e})  LSE max diff {dl:.3e}")
+    say(f"[lazy vs eager] O max diff {d:.3e} (max excess over the rounding bound {excess:.3e})  "
+        f"LSE max diff {dl:.3e}")
     assert excess <= 0.0 and dl <= TOL_LSE

@@ -25,25 +25,34 @@
 //     O^T = V^T P^T; V^T comes from ds_read_b64_tr_b16 transpose reads;
 //   * the O^T accumulators also hold one query row per lane, so the rescale factor
 //     is a per-lane scalar.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
 template <int D, int NQT, bool CAUSAL, bool VARLEN, int POLY, int TAU>
-__global__ __launch_bounds__(256 * NQT) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   constexpr int BN = kFwdBlockN;
   constexpr int NW = 4 * NQT;
   constexpr int WG_ROWS = kFwdTileRows * NQT;
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
   constexpr int TILE_BYTES = BN * ROWB;       // one K or V tile
-  constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K + V
   constexpr int SLOTS = D / 8;                // 16-byte slots per row
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NDS = D / 16;                 // k-steps of the QK product
   constexpr int NDB = D / 32;                 // 32-wide blocks of head_dim
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  // Two K buffers and two V buffers (K runs one tile ahead of V), declared as
+  // separate objects: the compiler can then tell that the buffers a step reads are
+  // not the ones its DMA loads are filling, and does not make the reads wait for
+  // those loads.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
+  auto kbuf = [&](int par) { return (FA_LDS char*)(par ? k_lds1 : k_lds0); };
+  auto vbuf = [&](int par) { return (FA_LDS char*)(par ? v_lds1 : v_lds0); };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,152 +113,235 @@ __global__ __launch_bounds__(256 * NQT) void fwd_kernel(FwdParams p) {
   if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + WG_ROWS));
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  // ---- K/V stage loader: every wave issues its share of 1 KiB DMA packets ----
-  auto issue_tile = [&](int t, int stage) {
+  // ---- tile loaders: every wave issues its share of 1 KiB DMA packets ----
+  auto issue = [&](const rsrc_t& rsrc, uint32_t ss2, int t, FA_LDS char* dst) {
     const int k0 = t * BN;
-    FA_LDS char* kd = smem + stage * STAGE_BYTES;
-    FA_LDS char* vd = kd + TILE_BYTES;
 #pragma unroll
     for (int i = wave; i < TILE_BYTES / 1024; i += NW) {
       const int idx = i * 64 + lane;
       const int r = idx / SLOTS;
-      const int c = (idx % SLOTS) ^ slot_swizzle<D>(r);
-      buf_load_lds16(rk, kd + i * 1024, (uint32_t)(k0 + r) * k_ss2 + c * 16);
-      buf_load_lds16(rv, vd + i * 1024, (uint32_t)(k0 + r) * v_ss2 + c * 16);
+      const int cs = (idx % SLOTS) ^ slot_swizzle<D>(r);
+      buf_load_lds16(rsrc, dst + i * 1024, (uint32_t)(k0 + r) * ss2 + cs * 16);
     }
   };
 
-  // lane-constant parts of the LDS operand addresses
+  // lane-constant LDS offsets within a tile buffer: with the buffer index a
+  // compile-time constant every K/V read is one register plus an immediate
   const int sw_k = slot_swizzle<D>(lane & 15);                    // K rows 32kb + (lane&31)
   const int i16 = lane & 15;
   const int vr1 = 4 * hl + (i16 >> 2);                             // V rows (mod 16) of the tr reads
   const int sw_v1 = slot_swizzle<D>(vr1), sw_v2 = slot_swizzle<D>(vr1 + 8);
   const int vc_lo = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);      // chunk within a 32-d block
   const int vhalf = (i16 & 1) * 8;
+  int off_k[NDS], off_v1[NDB], off_v2[NDB];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) off_k[ds] = (lane & 31) * ROWB + (((2 * ds + hl) ^ sw_k) << 4);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int cc = 4 * db + vc_lo;
+    off_v1[db] = vr1 * ROWB + ((cc ^ sw_v1) << 4) + vhalf;
+    off_v2[db] = (vr1 + 8) * ROWB + ((cc ^ sw_v2) << 4) + vhalf;
+  }
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_used = -INFINITY;
+  float mref = 0.0f;    // m_used * c once a row has seen a key
   float lsum = 0.0f;    // sum of fp32 weights
   float lsum_r = 0.0f;  // sum of bf16-rounded weights
   const float c = p.scale_log2;
 
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
-  // last tile; it then only helps stage K/V (second loop) and keeps the barriers.
+  // last tile; it then only helps stage K/V and keeps the barriers.
   int n_mine = n_tiles;
   if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 31) / BN + 1);
-  if (n_tiles > 0) issue_tile(0, 0);
-  int t = 0;
-  for (; t < n_mine; ++t) {
-    const int stage = t & 1;
+
+  // ---- one pipelined step j: S(j) = K(j) Q^T runs on the matrix cores while the
+  // weights of tile j-1 are exponentiated; then O^T += V(j-1)^T P(j-1)^T runs
+  // while the row maxima of S(j) are reduced.  Each wave's instruction stream thus
+  // alternates matrix and vector work: a few vector instructions issued after an
+  // MFMA run while it executes, and the other wave on the SIMD fills the rest.
+  // K(j) sits in K buffer j&1, V(j-1) in V buffer (j-1)&1; the loads of K(j+1) and
+  // V(j) are issued after the barrier that opens step j and waited for at the
+  // barrier that opens step j+1.
+  auto step = [&](const int j, auto par_c, auto prev_c, auto next_c, auto mask_c, f32x16(&s_prev)[NKB],
+                  f32x16(&s_next)[NKB]) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr bool PREV = decltype(prev_c)::value;  // tile j-1 exists: softmax + PV
+    constexpr bool NEXT = decltype(next_c)::value;  // tile j exists for this wave: S + max
+    constexpr bool MASK = decltype(mask_c)::value;  // tile j may hold keys this wave must not see
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
-    const int k0 = t * BN;
+    if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(PAR ^ 1));
+    if (j < n_tiles) issue(rv, v_ss2, j, vbuf(PAR));
+    const FA_LDS char* kt = kbuf(PAR);
+    const FA_LDS char* vt = vbuf(PAR ^ 1);
+    const int k0 = j * BN;
 
-    const FA_LDS char* kt = smem + stage * STAGE_BYTES;
-    const FA_LDS char* vt = kt + TILE_BYTES;
-
-    // S^T = K Q^T : lane holds query my_row, keys k0 + 32kb + 8(r/4) + 4hl + (r&3)
-    f32x16 sacc[NKB];
+    // -- phase 1, one 32-key block at a time: the NDS MFMAs of S(j)'s block kb, each
+    // followed by 16/NDS exponentials of tile j-1's block kb (with their sums and
+    // bf16 packing), so the previous scores die as the new ones appear --
+    constexpr int UPD = 8 / NDS;  // pairs of scores per MFMA
+    u32x4 pb[2 * NKB];
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four partial sums: short dependency chains
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) {
+      if constexpr (NEXT) s_next[kb] = f32x16{};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int coff = ((2 * ds + hl) ^ sw_k) << 4;
+      for (int ds = 0; ds < NDS; ++ds) {
+        if constexpr (NEXT) {
+          const u32x4 a = lds_read16(kt + 32 * kb * ROWB + off_k[ds]);
+          s_next[kb] = mfma_bf16(a, qreg[ds], s_next[kb]);
+        }
+        if constexpr (PREV) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a = lds_read16(kt + (32 * kb + (lane & 31)) * ROWB + coff);
-        sacc[kb] = mfma_bf16(a, qreg[ds], sacc[kb]);
+          for (int uu = 0; uu < UPD; ++uu) {
+            // P = 2^(s*c - m*c) -> bf16 operands; the fp32 weights feed the LSE sum
+            const int u = ds * UPD + uu;
+            const int e = 2 * u;
+            const float x0 = __builtin_fmaf(s_prev[kb][e], c, -mref);
+            const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref);
+            const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
+            const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
+            rs[u & 3] += p0;
+            rs[u & 3] += p1;
+            pb[2 * kb + (u >> 2)][u & 3] = pack_bf16(p0, p1);
+          }
+        }
+      }
+      if constexpr (NEXT && PREV) {
+        // keep the interleave: K reads run three MFMAs ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7 * UPD, 0);
+          if (ds < NDS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
+    if constexpr (PREV) lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
-    // mask: causal diagonal tiles and the ragged last tile only
-    bool need_mask = (k0 + BN > Lk);
-    if constexpr (CAUSAL) need_mask = need_mask || (k0 + BN - 1 > q0);
-    if (need_mask) {
+    // mask S(j) (the diagonal tiles under the causal mask and the ragged last tile)
+    if constexpr (NEXT && MASK) {
+      // key k0 + 4hl + rel is hidden when rel >= lim (one register; rel is a constant)
+      int lim = Lk;
+      if constexpr (CAUSAL) lim = min(lim, my_row + 1);
+      lim -= k0 + 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          bool hide = key >= Lk;
-          if constexpr (CAUSAL) hide = hide || key > my_row;
-          if (hide) sacc[kb][r] = -INFINITY;
+          const int rel = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s_next[kb][r] = rel >= lim ? -INFINITY : s_next[kb][r];
         }
     }
 
-    // row maximum of this tile (lane-local, then across the two wave halves)
+    // -- phase 2: O^T += V^T P^T, each MFMA followed by a step of the row-sum of the
+    // rounded weights or of the row maximum of S(j) --
     float mx = -INFINITY;
+    if constexpr (PREV) {
+      float rsr[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int g = 0; g < BN / 16; ++g) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = half_swap_max(mx);
-
-    // lazy rescale: move the reference only when the maximum grew by more than TAU
-    const float m_new = fmaxf(m_used, mx);
-    bool need = m_new > m_used;
-    if constexpr (TAU > 0) need = need && (m_used == -INFINITY || (m_new - m_used) * c > (float)TAU);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? (m_used == -INFINITY ? 0.0f : exp2_hw((m_used - m_new) * c)) : 1.0f;
-      m_used = need ? m_new : m_used;
-      lsum *= alpha;
-      lsum_r *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+          const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
+          const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
+          oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
+          // sum of the bf16-rounded weights the product used: O is normalised by
+          // it, so a dominant weight's rounding cancels between numerator and
+          // denominator (with a stale reference that weight is up to 2^8, not 1)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+          for (int e = db * 4 / NDB; e < (db + 1) * 4 / NDB; ++e) rsr[e & 1] = add_bf16_pair(pb[g][e], rsr[e & 1]);
+          if constexpr (NEXT) {
+            // two scores of S(j) per MFMA, 32 in all
+            const int i = g * NDB + db;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-
-    // P = 2^(s*c - m*c) -> bf16 operands.  Two row sums: of the fp32 weights (for
-    // the LSE) and of the bf16-rounded weights the PV product actually uses (for
-    // normalising O, so a dominant weight's rounding cancels between numerator and
-    // denominator; with a stale reference that weight is up to 2^8, not 1).
-    const float mref = (m_used == -INFINITY) ? 0.0f : m_used * c;
-    float rs = 0.0f, rsr = 0.0f;
-    u32x4 pb[2 * NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_fmaf(sacc[kb][r], c, -mref);
-        pv[r] = (r < POLY) ? exp2_poly(x) : exp2_hw(x);
-        rs += pv[r];
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = pack_bf16(pv[8 * half + 2 * e], pv[8 * half + 2 * e + 1]);
-          rsr = add_bf16_pair(w[e], rsr);
+            for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
+              mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_next[q >> 4][q & 15], s_next[q >> 4][(q & 15) + 1]));
+          }
         }
-        pb[2 * kb + half] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < BN / 16 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        if (i < BN / 16 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      lsum_r += rsr[0] + rsr[1];
+    } else if constexpr (NEXT) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s_next[kb][r]);
+    }
+
+    if constexpr (NEXT) {
+      // row maximum across the two wave halves; lazy rescale: move the reference
+      // only when the maximum grew by more than TAU.  O and the sums then hold
+      // everything up to tile j-1 and are scaled before tile j's weights are added.
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_used, mx);
+      bool need = m_new > m_used;
+      if constexpr (TAU > 0) need = need && (m_used == -INFINITY || (m_new - m_used) * c > (float)TAU);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? (m_used == -INFINITY ? 0.0f : exp2_hw((m_used - m_new) * c)) : 1.0f;
+        m_used = need ? m_new : m_used;
+        mref = (m_used == -INFINITY) ? 0.0f : m_used * c;
+        lsum *= alpha;
+        lsum_r *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
     }
-    lsum += rs;
-    lsum_r += rsr;
+  };
 
-    // O^T += V^T P^T : A operand = V^T through the transpose reads
-#pragma unroll
-    for (int g = 0; g < BN / 16; ++g) {
-      const int r1 = 16 * g + vr1;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int cc = 4 * db + vc_lo;
-        const u32x2 lo = lds_read_tr16(vt + r1 * ROWB + ((cc ^ sw_v1) << 4) + vhalf);
-        const u32x2 hi = lds_read_tr16(vt + (r1 + 8) * ROWB + ((cc ^ sw_v2) << 4) + vhalf);
-        oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
-      }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BF = std::false_type;
+  using BT = std::true_type;
+  using MF = std::false_type;
+  using MT = std::true_type;
+  // tiles before j_plain need no mask for this wave's rows
+  int j_plain = Lk / BN;
+  if constexpr (CAUSAL) j_plain = min(j_plain, (q0 + 1) / BN);
+  const int j_lim = min(n_mine, j_plain);
+  f32x16 sa[NKB], sb[NKB];
+  if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
+  int j = 0;
+  if (n_mine > 0) {
+    step(0, I0{}, BF{}, BT{}, MT{}, sb, sa);
+    j = 1;
+    for (; j + 1 < j_lim; j += 2) {  // j odd
+      step(j, I1{}, BT{}, BT{}, MF{}, sa, sb);
+      step(j + 1, I0{}, BT{}, BT{}, MF{}, sb, sa);
+    }
+    // the remaining tiles (masked when needed), then the last step
+    for (; j + 1 < n_mine; j += 2) {  // j odd
+      step(j, I1{}, BT{}, BT{}, MT{}, sa, sb);
+      step(j + 1, I0{}, BT{}, BT{}, MT{}, sb, sa);
+    }
+    if (j < n_mine) {
+      step(j, I1{}, BT{}, BT{}, MT{}, sa, sb);
+      step(j + 1, I0{}, BT{}, BF{}, MF{}, sb, sa);
+      j += 2;
+    } else {
+      step(j, I1{}, BT{}, BF{}, MF{}, sa, sb);
+      j += 1;
     }
   }
-  for (; t < n_tiles; ++t) {
+  // steps past this wave's last tile: barriers and loads only
+  for (; j <= n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, (t & 1) ^ 1);
+    const int par = j & 1;
+    if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(par ^ 1));
+    if (j < n_tiles) issue(rv, v_ss2, j, vbuf(par));
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l ----
