@@ -26,11 +26,39 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "headline"       # causal B=2 H=16 S=8192 d=128
+COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
 BWD_SEED_CONFIG = "c5"      # same shape with dO
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_causal_B2_H16_S8192_d128_hbm_traffic.md")
+
+
+def recorded_traffic(phase: str):
+    """HBM-side bytes per launch (read + written) of a kernel, from the committed
+    counter summary (FETCH_SIZE / WRITE_SIZE scaled by a copy of known size); None
+    when there is no record or the kernel's sources changed since it was taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_PROFILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if not ln.startswith("traffic-record: "):
+            continue
+        rec = json.loads(ln[len("traffic-record: "):])
+        if rec["phase"] != phase:
+            continue
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, "tiled_exact_attention_bf16_amd", "csrc", f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["read_bytes"]) + int(rec["write_bytes"])
+    return None
 
 
 def cpu_baseline(inp, budget_s: float = 12.0, max_heads: int = 8):
@@ -73,6 +101,8 @@ def main():
     ap.add_argument("--q-tiles", type=int, default=-1)
     ap.add_argument("--poly", type=int, default=-1)
     ap.add_argument("--tau", type=int, default=-1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch a plain device copy of a known size (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -134,6 +164,14 @@ def main():
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_calibration:
+        # outside the timed region: one copy kernel reading and writing COPY_BYTES
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {COPY_BYTES} bytes read and written")
     per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
     step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)]))
@@ -181,7 +219,7 @@ def main():
         "kernel_ms": {n: round(per[n], 4) for n in names},
         "roofline": {"bound": "mfma", "kernel": kernel_names[dominant], "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(dominant) if det or dominant == "fwd" else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
