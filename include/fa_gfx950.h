@@ -101,8 +101,12 @@ typedef struct fa_fwd_tuning {
    * more than this.  Compiled: 8 (the method) and 0 (eager).  -1 = default (8). */
   int32_t rescale_threshold_log2;
   /* Query tiles of 128 rows interleaved per workgroup (two wave sets sharing each
-   * K/V stage).  Compiled: 1, 2.  -1 = default. */
+   * K/V stage).  Compiled: 1, 2.  -1 = default.  Must be 2 or -1 with 64-row waves. */
   int32_t q_tiles_per_workgroup;
+  /* Query rows per wave: 32 (two waves per SIMD, 32x32 tiles) or 64 (one wave per
+   * SIMD owning two 32-row blocks, each K/V fragment read once for both; 256-row
+   * workgroups).  0 or negative = default. */
+  int32_t rows_per_wave;
 } fa_fwd_tuning;
 
 /* Bytes of device workspace fa_fwd needs for `a` (0 for fixed length; variable

@@ -94,6 +94,8 @@ def test_forward_validation(mutate, expect):
     ((2, 0, -1), L.FA_ERR_UNSUPPORTED),
     ((-1, 5, -1), L.FA_ERR_UNSUPPORTED),
     ((-1, -1, 3), L.FA_ERR_UNSUPPORTED),
+    ((-1, -1, -1, 48), L.FA_ERR_UNSUPPORTED),
+    ((-1, -1, 1, 64), L.FA_ERR_UNSUPPORTED),   # 64-row waves come in 256-row workgroups only
 ])
 def test_forward_tuning_validation(tuning, expect):
     assert fwd_status(fwd_args(), L.FwdTuning(*tuning)) == expect
@@ -104,6 +106,8 @@ def test_tile_rows():
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 1))) == 128
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 2))) == 256
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 7))) == 0
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, -1, 64))) == 256
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 1, 64))) == 0
 
 
 def varlen_args(n_seq=32, total=131072, max_len=16384, causal=1, h=16, d=128):

@@ -40,34 +40,42 @@ def check_heads(inp, o, lse, pairs, rows=None, tag="", strict=False):
     return worst
 
 
+# both wave layouts: 32 query rows per wave (two waves per SIMD) and 64 (one per SIMD)
+RPW = [32, 64]
+
+
+@pytest.mark.parametrize("rpw", RPW)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("s", [1, 2, 17, 127, 128, 129, 255, 256, 1000])
-def test_small_shapes(s, causal, d):
+def test_small_shapes(s, causal, d, rpw):
     inp = I.random_inputs(100 + s, 2, s, 3, d, causal)
-    say(f"case s={s} causal={causal} d={d}")
-    o, lse = run_fwd(inp)
-    check_heads(inp, o, lse, [(b, h) for b in range(2) for h in range(3)], tag=f"s{s}c{int(causal)}d{d}")
+    say(f"case s={s} causal={causal} d={d} rows/wave={rpw}")
+    o, lse = run_fwd(inp, FA.Tuning(rows_per_wave=rpw))
+    check_heads(inp, o, lse, [(b, h) for b in range(2) for h in range(3)], tag=f"s{s}c{int(causal)}d{d}w{rpw}")
 
 
-@pytest.mark.parametrize("variant", [(0, 8, 1), (0, 8, 2), (2, 8, 2), (4, 8, 2), (2, 8, 1), (0, 0, 2), (0, 0, 1)])
+@pytest.mark.parametrize("variant", [(0, 8, 1, 32), (0, 8, 2, 32), (2, 8, 2, 32), (4, 8, 2, 32), (2, 8, 1, 32),
+                                     (0, 0, 2, 32), (0, 0, 1, 32), (0, 8, 2, 64), (2, 8, 2, 64), (4, 8, 2, 64),
+                                     (0, 0, 2, 64)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_variants_with_wide_logits(variant, causal):
     # Q ~ N(0, 3^2): row maxima grow across key tiles, so lazy rescales fire
-    poly, tau, qt = variant
+    poly, tau, qt, rpw = variant
     inp = I.random_inputs(7, 1, 700, 4, 128, causal, q_std=3.0)
     say(f"case variant={variant} causal={causal}")
-    o, lse = run_fwd(inp, FA.Tuning(poly, tau, qt))
+    o, lse = run_fwd(inp, FA.Tuning(poly, tau, qt, rpw))
     check_heads(inp, o, lse, [(0, h) for h in range(4)], tag=f"variant{variant}c{int(causal)}")
 
 
+@pytest.mark.parametrize("rpw", RPW)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_varlen_ragged_with_empty_and_single(causal, d):
+def test_varlen_ragged_with_empty_and_single(causal, d, rpw):
     lens = [0, 1, 5, 128, 129, 300, 17, 0, 256, 511]
     inp = I.random_varlen_inputs(11, lens, heads=2, head_dim=d, causal=causal)
-    say(f"case varlen causal={causal} d={d}")
-    o, lse = run_fwd(inp)
+    say(f"case varlen causal={causal} d={d} rows/wave={rpw}")
+    o, lse = run_fwd(inp, FA.Tuning(rows_per_wave=rpw))
     check_heads(inp, o, lse, [(b, h) for b in range(len(lens)) for h in range(2)], tag=f"varlen{d}")
 
 
@@ -77,11 +85,12 @@ def test_config_c1_full():
     check_heads(inp, o, lse, [(0, 0), (0, 1)], tag="c1", strict=True)
 
 
+@pytest.mark.parametrize("rpw", RPW)
 @pytest.mark.parametrize("name", ["c2", "c2_causal", "headline"])
-def test_configs_sampled_heads(name):
+def test_configs_sampled_heads(name, rpw):
     inp = I.make_inputs(name)
-    say(f"case {name}")
-    o, lse = run_fwd(inp)
+    say(f"case {name} rows/wave={rpw}")
+    o, lse = run_fwd(inp, FA.Tuning(rows_per_wave=rpw))
     assert bool(torch.isfinite(o).all()) and not bool(torch.isnan(lse).any())
     pairs = [(0, 0), (inp.batch - 1, inp.num_heads - 1), (1 % inp.batch, 5 % inp.num_heads)]
     check_heads(inp, o, lse, pairs, tag=name, strict=True)

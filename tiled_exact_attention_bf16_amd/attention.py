@@ -17,14 +17,16 @@ from . import _lib as L
 
 @dataclass
 class Tuning:
-    """Forward variant: FMA-exp2 share (of 16), lazy threshold (log2 units), query tiles per workgroup.
-    -1 keeps the library default."""
+    """Forward variant: FMA-exp2 share (of 16), lazy threshold (log2 units), query tiles per
+    workgroup, query rows per wave (32 or 64).  -1 keeps the library default."""
     exp2_poly_per16: int = -1
     rescale_threshold_log2: int = -1
     q_tiles_per_workgroup: int = -1
+    rows_per_wave: int = -1
 
     def c(self):
-        return L.FwdTuning(self.exp2_poly_per16, self.rescale_threshold_log2, self.q_tiles_per_workgroup)
+        return L.FwdTuning(self.exp2_poly_per16, self.rescale_threshold_log2, self.q_tiles_per_workgroup,
+                           self.rows_per_wave)
 
 
 def _ptr(t: Optional[torch.Tensor]):

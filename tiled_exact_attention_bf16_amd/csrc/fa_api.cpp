@@ -90,18 +90,22 @@ fa_status check_tensor(const void* ptr, const int64_t st[3], const Shape& s, int
 int fwd_max_items(const Shape& s, int tile_rows) { return (s.total_q + tile_rows - 1) / tile_rows + s.batch; }
 
 struct FwdChoice {
-  int poly, tau, qt;
+  int poly, tau, qt, rpw;
 };
 
 fa_status pick_tuning(const fa_fwd_tuning* t, FwdChoice* c) {
   c->poly = 0;
   c->tau = 8;
   c->qt = 2;
+  c->rpw = 32;
   if (t == nullptr) return FA_OK;
   if (t->exp2_poly_per16 >= 0) c->poly = t->exp2_poly_per16;
   if (t->rescale_threshold_log2 >= 0) c->tau = t->rescale_threshold_log2;
   if (t->q_tiles_per_workgroup >= 0) c->qt = t->q_tiles_per_workgroup;
+  if (t->rows_per_wave > 0) c->rpw = t->rows_per_wave;
   if (c->qt != 1 && c->qt != 2) return FA_ERR_UNSUPPORTED;
+  if (c->rpw != 32 && c->rpw != 64) return FA_ERR_UNSUPPORTED;
+  if (c->rpw == 64 && c->qt != 2) return FA_ERR_UNSUPPORTED;
   if (c->tau == 8 && (c->poly == 0 || c->poly == 2 || c->poly == 4)) return FA_OK;
   if (c->tau == 0 && c->poly == 0) return FA_OK;
   return FA_ERR_UNSUPPORTED;
@@ -215,7 +219,7 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
   fa::FwdParams p = make_fwd_params(a, s);
   p.n_qtiles = s.varlen ? 0 : (s.max_q + tile_rows - 1) / tile_rows;
   p.sched = (const int32_t*)workspace;
-  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau};
+  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, c.rpw};
   hipStream_t strm = (hipStream_t)stream;
   if (s.varlen) {
     hipError_t e = fa::launch_fwd_schedule(s.cu_q, s.cu_k, s.batch, tile_rows, fa::kFwdBlockN, cfg.causal,

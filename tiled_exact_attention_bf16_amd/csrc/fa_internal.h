@@ -41,6 +41,7 @@ struct FwdConfig {
   bool varlen;
   int poly_per16;   // 0, 2, 4
   int tau;          // 8 or 0
+  int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd64_kernel, q_tiles == 2)
 };
 
 // Returns hipSuccess or the launch error.  Grid size is derived from p and cfg.
