@@ -90,6 +90,56 @@ def cpu_baseline(inp, budget_s: float = 12.0, max_heads: int = 8):
                       f"{inp.q.shape[1]}-token causal workload, {t_total:.1f} s"}
 
 
+def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
+    """Forward and backward TFLOP/s of every named workload: median and min over
+    `iters` timed calls (HIP events on the library's stream) after `warmup` calls."""
+    import torch
+    from tiled_exact_attention_bf16_amd import attention as FA
+    from tiled_exact_attention_bf16_amd import inputs as I
+    from tiled_exact_attention_bf16_amd import workload as W
+    res = {}
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    for name in ("c1", "c2", "c2_causal", "c3", "c4", "headline", "c5"):
+        inp = I.make_inputs(name)
+        log(f"[bench] config {name}")
+        q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+        if inp.do is not None:
+            do = dev(inp.do)
+        else:  # timing only: dO values do not change the work
+            g = torch.Generator(device="cuda").manual_seed(inp.seed + 1000)
+            do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+        cu = torch.from_numpy(inp.cu_seqlens).cuda() if inp.varlen else None
+        mx = inp.max_seqlen() if inp.varlen else None
+        lens = [int(x) for x in inp.seqlens()]
+        f_fwd = W.fwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal)
+        f_bwd = W.bwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal)
+        o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx)
+        dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in (q, k, v))
+        run = {"fwd": lambda: FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx,
+                                     out=o, lse=lse),
+               "bwd": lambda: FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, cu_seqlens_q=cu,
+                                     max_seqlen_q=mx, deterministic=deterministic, dq=dq, dk=dk, dv=dv)}
+        row = {}
+        for ph, fn in run.items():
+            for _ in range(warmup):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in ev])
+            flop = f_fwd if ph == "fwd" else f_bwd
+            row[ph] = {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(ms.min()), 4),
+                       "tflops_median": round(flop / (np.median(ms) * 1e-3) / 1e12, 2),
+                       "tflops_max": round(flop / (ms.min() * 1e-3) / 1e12, 2)}
+        res[name] = row
+        del q, k, v, do, o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +152,8 @@ def main():
     ap.add_argument("--poly", type=int, default=-1)
     ap.add_argument("--tau", type=int, default=-1)
     ap.add_argument("--rows-per-wave", type=int, default=-1)
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time forward and backward of every named workload (median/min of 50)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain device copy of a known size (for scaling HBM counters)")
     args = ap.parse_args()
@@ -222,6 +274,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dominant) if det or dominant == "fwd" else None},
     }
+    if args.all_configs:
+        out["configs"] = time_all_configs(det)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(inp)
