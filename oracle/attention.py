@@ -19,9 +19,12 @@ splitting the query rows into independent blocks to bound memory):
       LSE_i = m_i + ln sum_j exp(s_ij - m_i)      (natural log, scale included)
 
   Masks (fdeinterviews.com FA4 summary, features paragraph: causal masks and
-  variable lengths):  causal hides keys j > i (top-left aligned; used only with
-  equal query and key lengths); variable length restricts attention to the keys
-  of the query's own sequence.  A query that sees no key gets O = 0, LSE = -inf.
+  variable lengths):  causal hides key j from query i when j > i + (Lk - Lq), so
+  that the last query sees every key (the diagonal is aligned to the bottom-right
+  corner; with Lq = Lk this is the usual j > i, and with Lq < Lk the queries are
+  the last Lq positions of the key sequence, as in generation with a cache);
+  variable length restricts attention to the keys of the query's own sequence.
+  A query that sees no key gets O = 0, LSE = -inf.
 
   Backward (the gradient of the forward above; the pages name a backward pass
   and its dQ accumulation but print no equations), from the exact P:
@@ -44,12 +47,13 @@ import numpy as np
 ROW_BLOCK = 512
 
 
-def _mask_block(s: np.ndarray, rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray:
-    """Return a boolean array, True where key j is visible to the query in ``rows``."""
+def _mask_block(rows: np.ndarray, n_queries: int, n_keys: int, causal: bool) -> np.ndarray:
+    """Return a boolean array, True where key j is visible to the query in ``rows``
+    (causal: j <= row + n_keys - n_queries)."""
     if not causal:
         return np.ones((len(rows), n_keys), dtype=bool)
     keys = np.arange(n_keys)
-    return keys[None, :] <= rows[:, None]
+    return keys[None, :] <= rows[:, None] + (n_keys - n_queries)
 
 
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
@@ -73,7 +77,7 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
     for b0 in range(0, len(row_idx), ROW_BLOCK):
         r = row_idx[b0:b0 + ROW_BLOCK]
         s = scale * (q[r] @ k.T)
-        vis = _mask_block(s, r, lk, causal)
+        vis = _mask_block(r, lq, lk, causal)
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
         seen = np.isfinite(m)
@@ -92,7 +96,7 @@ def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool)
     k = np.asarray(k, dtype=np.float64)
     rows = np.arange(q.shape[0])
     s = float(scale) * (q @ k.T)
-    s = np.where(_mask_block(s, rows, k.shape[0], causal), s, -np.inf)
+    s = np.where(_mask_block(rows, q.shape[0], k.shape[0], causal), s, -np.inf)
     m = s.max(axis=1)
     seen = np.isfinite(m)
     e = np.exp(s - np.where(seen, m, 0.0)[:, None])
@@ -123,7 +127,7 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     for b0 in range(0, lq, ROW_BLOCK):
         r = np.arange(b0, min(lq, b0 + ROW_BLOCK))
         s = scale * (q[r] @ k.T)
-        vis = _mask_block(s, r, lk, causal)
+        vis = _mask_block(r, lq, lk, causal)
         seen = np.isfinite(lse[r])
         p = np.where(vis & seen[:, None], np.exp(s - np.where(seen, lse[r], 0.0)[:, None]), 0.0)
         dv += p.T @ do[r]

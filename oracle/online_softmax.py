@@ -63,7 +63,7 @@ def tiled_head_forward(q, k, v, scale: float, causal: bool, block_k: int, tau: f
     for k0 in starts:
         kk = np.arange(k0, min(lk, k0 + block_k))
         s = (q @ k[kk].T).astype(dtype)
-        visible = np.ones_like(s, dtype=bool) if not causal else (kk[None, :] <= rows[:, None])
+        visible = np.ones_like(s, dtype=bool) if not causal else (kk[None, :] <= rows[:, None] + (lk - lq))
         s = np.where(visible, s, dtype(-np.inf))
         tile_max = s.max(axis=1)                       # -inf when nothing is visible
         has = np.isfinite(tile_max)

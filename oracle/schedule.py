@@ -27,8 +27,9 @@ def item_cost(row0: int, block_m: int, seqlen_q: int, seqlen_k: int, block_n: in
     if not causal:
         keys = seqlen_k
     else:
+        # bottom-right causal alignment: row i sees keys j <= i + seqlen_k - seqlen_q
         last_row = min(row0 + block_m, seqlen_q) - 1
-        keys = min(last_row + 1, seqlen_k)
+        keys = max(0, min(last_row + 1 + seqlen_k - seqlen_q, seqlen_k))
     return -(-keys // block_n)
 
 

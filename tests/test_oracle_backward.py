@@ -86,3 +86,24 @@ def test_varlen_packing_invariance():
         g = A.backward(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], do[None, s0:s1], inp.scale, True)
         for full, part in zip((dq, dk, dv), g):
             assert np.array_equal(full[s0:s1], part[0])
+
+
+@pytest.mark.parametrize("lq,lk", [(9, 40), (40, 9), (1, 17)])
+def test_bottom_right_causal_against_torch_autograd(lq, lk):
+    """Unequal lengths under the causal mask: torch's lower-right causal bias with
+    float64 autograd (rows that see no key contribute nothing)."""
+    from torch.nn.attention.bias import causal_lower_right
+    d = 8
+    q, do = _rand((lq, d), 70), _rand((lq, d), 71)
+    k, v = _rand((lk, d), 72), _rand((lk, d), 73)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = A.head_backward(q, k, v, do, scale, True)
+    seen = np.arange(lq) + lk - lq >= 0
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
+                                                         attn_mask=causal_lower_right(lq, lk), scale=scale)[0, 0]
+    o = torch.where(torch.from_numpy(seen)[:, None], o, torch.zeros_like(o))   # torch gives NaN rows there
+    o.backward(torch.from_numpy(do))
+    assert np.all(dq[~seen] == 0.0)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(mine - np.nan_to_num(ref.numpy()))) <= 1e-11

@@ -165,7 +165,7 @@ def test_brute_force_loops(causal, n, d):
 @pytest.mark.parametrize("lq,lk,d", [(33, 33, 16), (64, 64, 64), (5, 70, 8)])
 def test_against_torch_float64(causal, lq, lk, d):
     if causal and lq != lk:
-        pytest.skip("causal is defined for equal query and key lengths")
+        pytest.skip("rectangular causal: see test_bottom_right_causal_against_torch")
     q, k, v = _rand((lq, d), 40, 2.0), _rand((lk, d), 41), _rand((lk, d), 42)
     scale = 1.0 / math.sqrt(d)
     o, lse = A.head_forward(q, k, v, scale, causal)
@@ -176,3 +176,42 @@ def test_against_torch_float64(causal, lq, lk, d):
     if causal:
         s = s.masked_fill(torch.triu(torch.ones(lq, lk, dtype=torch.bool), 1), float("-inf"))
     assert np.max(np.abs(lse - torch.logsumexp(s, dim=1).numpy())) <= 1e-12
+
+
+# --- causal with unequal query and key lengths (bottom-right alignment) ------------
+
+@pytest.mark.parametrize("lq,lk,d", [(5, 70, 8), (1, 33, 16), (17, 64, 32), (64, 17, 8), (2, 1, 4)])
+def test_bottom_right_causal_against_torch(lq, lk, d):
+    """torch's lower-right causal bias is an independent implementation of the
+    alignment (the last query sees every key)."""
+    from torch.nn.attention.bias import causal_lower_right
+    q, k, v = _rand((lq, d), 50, 2.0), _rand((lk, d), 51), _rand((lk, d), 52)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = A.head_forward(q, k, v, scale, True)
+    seen = np.isfinite(lse)
+    assert np.all(seen == (np.arange(lq) + lk - lq >= 0))
+    assert np.all(o[~seen] == 0.0)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(lq, lk),
+                                                           scale=scale)[0, 0].numpy()
+    assert np.max(np.abs(o[seen] - ref[seen])) <= 1e-12
+
+
+@pytest.mark.parametrize("lq,lk", [(7, 40), (40, 7), (1, 9)])
+def test_bottom_right_causal_is_the_tail_of_the_square_problem(lq, lk):
+    """With Lq < Lk the queries behave as the last Lq of Lk positions; with Lq > Lk
+    the last Lk queries behave as a square problem and the others see nothing."""
+    d = 8
+    k, v = _rand((lk, d), 60), _rand((lk, d), 61)
+    if lq <= lk:
+        full_q = _rand((lk, d), 62)
+        q = full_q[lk - lq:]
+        o_sq, lse_sq = A.head_forward(full_q, k, v, 0.7, True)
+        o, lse = A.head_forward(q, k, v, 0.7, True)
+        assert np.max(np.abs(o - o_sq[lk - lq:])) <= 1e-13 and np.max(np.abs(lse - lse_sq[lk - lq:])) <= 1e-13
+    else:
+        q = _rand((lq, d), 63)
+        o, lse = A.head_forward(q, k, v, 0.7, True)
+        o_sq, lse_sq = A.head_forward(q[lq - lk:], k, v, 0.7, True)
+        assert np.all(o[:lq - lk] == 0.0) and np.all(np.isneginf(lse[:lq - lk]))
+        assert np.max(np.abs(o[lq - lk:] - o_sq)) <= 1e-13 and np.max(np.abs(lse[lq - lk:] - lse_sq)) <= 1e-13
