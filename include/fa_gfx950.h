@@ -35,10 +35,12 @@
  *     contiguous for fixed length, [H, total_q] for variable length.
  *   - cu_seqlens arrays live in device memory, hold batch+1 non-decreasing int32
  *     entries starting at 0 and ending at total_q (total_k).  Their contents are
- *     trusted (not validated).  Variable-length causal attention requires equal
- *     query and key lengths per sequence (cu_seqlens_k == cu_seqlens_q or NULL).
- *   - Causal masking hides key j from query i when j > i (top-left aligned) and
- *     requires seqlen_q == seqlen_k.
+ *     trusted (not validated).
+ *   - Causal masking hides key j from query i (both counted from the start of
+ *     their sequence) when j > i + L_k - L_q: the mask's diagonal ends at the last
+ *     query and the last key (bottom-right alignment), which is the usual j > i
+ *     for equal lengths and puts L_q < L_k queries at the end of the key sequence,
+ *     as in generation with a cache.  Per sequence for variable length.
  *   - A query row that sees no key gets O = 0 and LSE = -inf.
  *   - NaN/Inf in the data are propagated, not checked.
  */

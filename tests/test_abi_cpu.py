@@ -76,7 +76,6 @@ def test_fixed_length_forward_needs_no_workspace():
     (lambda a: setattr(a, "softmax_scale", float("inf")), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "softmax_scale", -1.0), L.FA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "causal", 2), L.FA_ERR_INVALID_ARGUMENT),
-    (lambda a: (setattr(a, "causal", 1), setattr(a, "seqlen_k", 128)), L.FA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "q_stride", L.Strides(256 * 512, 500, 128)), L.FA_ERR_INVALID_ARGUMENT),  # stride % 8
     (lambda a: setattr(a, "o_stride", L.Strides(256 * 512, 64, 128)), L.FA_ERR_INVALID_ARGUMENT),   # rows overlap D
     (lambda a: setattr(a, "cu_seqlens_k", P), L.FA_ERR_INVALID_ARGUMENT),   # k offsets without q offsets
@@ -129,8 +128,8 @@ def test_varlen_workspace_and_checks():
     assert fwd_status(a, ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
     assert fwd_status(a, L.FwdTuning(-1, -1, 1), ws=P, ws_bytes=n - 256) == L.FA_ERR_WORKSPACE_TOO_SMALL
     assert fwd_status(a, ws=P + 16, ws_bytes=n) == L.FA_ERR_INVALID_ARGUMENT  # workspace alignment
-    a.cu_seqlens_k = P + 0x6000000                                          # causal needs shared offsets
-    assert fwd_status(a) == L.FA_ERR_UNSUPPORTED
+    a.cu_seqlens_k = P + 0x6000000        # separate key offsets under the causal mask (bottom-right)
+    assert ws_size(a)[0] == L.FA_OK
     b = varlen_args()
     b.cu_seqlens_q = P + 2                                                   # int32 alignment
     assert ws_size(b)[0] == L.FA_ERR_INVALID_ARGUMENT
@@ -176,13 +175,22 @@ def test_backward_workspace_sizes():
     assert st == L.FA_OK and rows * 4 <= n_det < n_atomic  # no accumulator in deterministic mode
 
 
+def test_causal_with_unequal_lengths_is_accepted():
+    # the causal mask aligns the diagonal to the bottom-right corner, so L_q != L_k is valid
+    a = fwd_args()
+    a.causal, a.seqlen_k = 1, 1000
+    assert ws_size(a) == (L.FA_OK, 0)
+    b = bwd_args()
+    b.seqlen_k = 100
+    assert bwd_ws(b)[0] == L.FA_OK
+
+
 @pytest.mark.parametrize("mutate,expect", [
     (lambda a: setattr(a, "dout", None), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "dq", P + 4), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "deterministic", 3), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "grad_dtype", 7), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "head_dim", 256), L.FA_ERR_UNSUPPORTED),
-    (lambda a: setattr(a, "seqlen_k", 100), L.FA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "dk_stride", L.Strides(256 * 512, 130, 128)), L.FA_ERR_INVALID_ARGUMENT),
 ])
 def test_backward_validation(mutate, expect):

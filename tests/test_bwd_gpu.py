@@ -54,6 +54,16 @@ def test_small_shapes(s, causal, d, deterministic):
 
 
 @pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("lq,lk", [(7, 300), (300, 129), (64, 1000), (1000, 64), (1, 257), (130, 200)])
+def test_causal_unequal_lengths(lq, lk, deterministic):
+    # bottom-right causal alignment; with lq > lk the first lq - lk rows see no key
+    inp = I.random_inputs(400 + lq + lk, 2, lq, 2, 128, True, with_do=True, seqlen_k=lk)
+    say(f"case causal lq={lq} lk={lk} det={deterministic}")
+    grads = run_fwd_bwd(inp, deterministic)
+    check_grads(inp, grads, [(b, h) for b in range(2) for h in range(2)], f"causal{lq}x{lk}det{int(deterministic)}")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
 def test_varlen_ragged(deterministic):
     lens = [0, 1, 5, 128, 129, 300, 17, 0, 256, 511]
     inp = I.random_varlen_inputs(12, lens, heads=2, head_dim=128, causal=True, with_do=True)

@@ -55,6 +55,17 @@ def test_small_shapes(s, causal, d, rpw):
     check_heads(inp, o, lse, [(b, h) for b in range(2) for h in range(3)], tag=f"s{s}c{int(causal)}d{d}w{rpw}")
 
 
+@pytest.mark.parametrize("rpw", RPW)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("lq,lk", [(1, 4096), (7, 1000), (128, 4096), (300, 257), (1000, 64), (64, 1000), (257, 300)])
+def test_causal_unequal_lengths(lq, lk, d, rpw):
+    # bottom-right causal alignment; with lq > lk the first lq - lk rows see no key
+    inp = I.random_inputs(300 + lq + lk, 2, lq, 2, d, True, seqlen_k=lk)
+    say(f"case causal lq={lq} lk={lk} d={d} rows/wave={rpw}")
+    o, lse = run_fwd(inp, FA.Tuning(rows_per_wave=rpw))
+    check_heads(inp, o, lse, [(b, h) for b in range(2) for h in range(2)], tag=f"causal{lq}x{lk}d{d}w{rpw}")
+
+
 @pytest.mark.parametrize("variant", [(0, 8, 1, 32), (0, 8, 2, 32), (2, 8, 2, 32), (4, 8, 2, 32), (2, 8, 1, 32),
                                      (0, 0, 2, 32), (0, 0, 1, 32), (0, 8, 2, 64), (2, 8, 2, 64), (4, 8, 2, 64),
                                      (0, 0, 2, 64)])

@@ -49,7 +49,6 @@ fa_status check_shape(int batch, int seqlen_q, int seqlen_k, int heads, int d, c
       total_k = total_q;
     }
     if (max_k < 0 || total_k < 0) return FA_ERR_INVALID_ARGUMENT;
-    if (causal && (cu_k != cu_q || total_k != total_q)) return FA_ERR_UNSUPPORTED;
     if (((uintptr_t)cu_q & 3u) || ((uintptr_t)cu_k & 3u)) return FA_ERR_INVALID_ARGUMENT;
     s.max_q = max_q;
     s.max_k = max_k;
@@ -58,7 +57,6 @@ fa_status check_shape(int batch, int seqlen_q, int seqlen_k, int heads, int d, c
   } else {
     if (cu_k != nullptr) return FA_ERR_INVALID_ARGUMENT;
     if (seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARGUMENT;
-    if (causal && seqlen_q != seqlen_k) return FA_ERR_UNSUPPORTED;
     s.varlen = false;
     s.max_q = seqlen_q;
     s.max_k = seqlen_k;

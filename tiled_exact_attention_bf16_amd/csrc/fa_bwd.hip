@@ -254,7 +254,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
     buf_load_lds16(rv, v_lds + i * 1024, (uint32_t)(k_blk0 + r) * v_ss2 + cc * 16);
   }
 
-  const int i_start = CAUSAL ? k_blk0 / BM : 0;
+  // causal: row i sees keys j <= i + coff (bottom-right alignment; 0 for equal lengths)
+  const int coff = Lk - Lq;
+  const int i_start = CAUSAL ? max(0, k_blk0 - coff) / BM : 0;
   const int i_end = (Lq + BM - 1) / BM;
   const int n_steps = i_end > i_start ? i_end - i_start : 0;
   const float c = p.scale_log2;
@@ -334,9 +336,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
 
     const int row0 = q0 + 32 * qh;   // first row of this wave's half
     // every key of the wave after every row of its half: nothing visible
-    const bool skip = CAUSAL && (k_blk0 + 32 * kw > row0 + 31);
+    const bool skip = CAUSAL && (k_blk0 + 32 * kw > row0 + 31 + coff);
     bool need_mask = (k_blk0 + BNK > Lk);
-    if constexpr (CAUSAL) need_mask = need_mask || (k_blk0 + 32 * kw + 31 > row0);
+    if constexpr (CAUSAL) need_mask = need_mask || (k_blk0 + 32 * kw + 31 > row0 + coff);
     u32x4 dsh[2], dsl[2];
     if (!skip) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
             if (need_mask) {
               const int query = row0 + 8 * r4 + 4 * hl + j;
               bool hide = my_key >= Lk;
-              if constexpr (CAUSAL) hide = hide || my_key > query;
+              if constexpr (CAUSAL) hide = hide || my_key > query + coff;
               pe = hide ? 0.0f : pe;
             }
             pv[j] = pe;
@@ -550,10 +552,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   }
 
   int kv_end = Lk;
-  if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + WG_ROWS));
+  const int coff = Lk - Lq;  // causal: row i sees keys j <= i + coff
+  if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
   const int n_tiles = (kv_end + BN - 1) / BN;
   int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 31) / BN + 1);
+  if constexpr (CAUSAL) n_mine = (q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
 
   auto issue_tile = [&](int t, int stage) {
     const int k0 = t * BN;
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     const FA_LDS char* kt = smem + stage * STAGE_BYTES;
     const FA_LDS char* vt = kt + TILE_BYTES;
     bool need_mask = (k0 + BN > Lk);
-    if constexpr (CAUSAL) need_mask = need_mask || (k0 + BN - 1 > q0);
+    if constexpr (CAUSAL) need_mask = need_mask || (k0 + BN - 1 > q0 + coff);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
             if (need_mask) {
               const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
               bool hide = key >= Lk;
-              if constexpr (CAUSAL) hide = hide || key > my_row;
+              if constexpr (CAUSAL) hide = hide || key > my_row + coff;
               pe = hide ? 0.0f : pe;
             }
             dv2[u] = pe * __builtin_fmaf(dp[r], p.scale, -dvs);   // scale * P (dP - D)
@@ -673,8 +676,9 @@ __global__ __launch_bounds__(1024) void sched_kv_kernel(const int32_t* cu_q, con
   __syncthreads();
   auto cost_of = [&](int b, int j) {
     const int lq = cu_q[b + 1] - cu_q[b];
+    const int lk = cu_k[b + 1] - cu_k[b];
     const int steps = (lq + kBwdBlockM - 1) / kBwdBlockM;
-    const int first = causal ? (j * kBwdBlockN) / kBwdBlockM : 0;
+    const int first = causal ? max(0, j * kBwdBlockN - (lk - lq)) / kBwdBlockM : 0;
     return min(max(steps - first, 0), kSchedMaxCost);
   };
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {

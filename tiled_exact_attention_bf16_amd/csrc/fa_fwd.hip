@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   for (int ds = 0; ds < NDS; ++ds) qreg[ds] = buf_load16(rq, (uint32_t)my_row * q_ss2 + (2 * ds + hl) * 16);
 
   int kv_end = Lk;
-  if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + WG_ROWS));
+  // causal: row i sees keys j <= i + coff (the mask's diagonal ends at the last query
+  // and the last key; coff = 0 for equal lengths)
+  const int coff = Lk - Lq;
+  if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   // ---- tile loaders: every wave issues its share of 1 KiB DMA packets ----
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
   // last tile; it then only helps stage K/V and keeps the barriers.
   int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 31) / BN + 1);
+  if constexpr (CAUSAL) n_mine = (q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
 
   // ---- one pipelined step j: S(j) = K(j) Q^T runs on the matrix cores while the
   // weights of tile j-1 are exponentiated; then O^T += V(j-1)^T P(j-1)^T runs
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     if constexpr (NEXT && MASK) {
       // key k0 + 4hl + rel is hidden when rel >= lim (one register; rel is a constant)
       int lim = Lk;
-      if constexpr (CAUSAL) lim = min(lim, my_row + 1);
+      if constexpr (CAUSAL) lim = min(lim, my_row + 1 + coff);
       lim -= k0 + 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   using MT = std::true_type;
   // tiles before j_plain need no mask for this wave's rows
   int j_plain = Lk / BN;
-  if constexpr (CAUSAL) j_plain = min(j_plain, (q0 + 1) / BN);
+  if constexpr (CAUSAL) j_plain = min(j_plain, max(0, q0 + 1 + coff) / BN);
   const int j_lim = min(n_mine, j_plain);
   f32x16 sa[NKB], sb[NKB];
   if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
@@ -459,7 +462,10 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
   }
 
   int kv_end = Lk;
-  if constexpr (CAUSAL) kv_end = min(Lk, min(Lq, wg_q0 + WG_ROWS));
+  // causal: row i sees keys j <= i + coff (the mask's diagonal ends at the last query
+  // and the last key; coff = 0 for equal lengths)
+  const int coff = Lk - Lq;
+  if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   auto issue = [&](const rsrc_t& rsrc, uint32_t ss2, int t, FA_LDS char* dst) {
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
   const float c = p.scale_log2;
 
   int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = min(n_tiles, (q0 + 63) / BN + 1);
+  if constexpr (CAUSAL) n_mine = (q0 + 63 + coff < 0) ? 0 : min(n_tiles, (q0 + 63 + coff) / BN + 1);
 
   // exponentials of two scores of a block's previous tile -> one packed bf16 pair
   auto weights2 = [&](const RowBlock<NDB>& X, const f32x16& s, int e, float& acc) -> uint32_t {
@@ -593,8 +599,8 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
     if constexpr (NEXT && MASK) {
       int lim_a = Lk, lim_b = Lk;
       if constexpr (CAUSAL) {
-        lim_a = min(lim_a, row_a + 1);
-        lim_b = min(lim_b, row_b + 1);
+        lim_a = min(lim_a, row_a + 1 + coff);
+        lim_b = min(lim_b, row_b + 1 + coff);
       }
       lim_a -= k0 + 4 * hl;
       lim_b -= k0 + 4 * hl;
@@ -670,7 +676,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
   using BF = std::false_type;
   using BT = std::true_type;
   int j_plain = Lk / BN;
-  if constexpr (CAUSAL) j_plain = min(j_plain, (q0 + 1) / BN);
+  if constexpr (CAUSAL) j_plain = min(j_plain, max(0, q0 + 1 + coff) / BN);
   const int j_lim = min(n_mine, j_plain);
   f32x16 sa0[NKB], sa1[NKB], sb0[NKB], sb1[NKB];
   if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const 
     const int lq = cu_q[b + 1] - cu_q[b];
     const int lk = cu_k[b + 1] - cu_k[b];
     int kv = lk;
-    if (causal) kv = min(lk, min(lq, (t + 1) * tile_rows));
+    if (causal) kv = max(0, min(lk, min(lq, (t + 1) * tile_rows) + lk - lq));
     return min((kv + block_n - 1) / block_n, kSchedMaxCost);
   };
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
