@@ -140,6 +140,45 @@ def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
     return res
 
 
+def time_decode(warmup: int = 10, iters: int = 50):
+    """Short queries against a long key sequence (generation with a cache): forward
+    time with the key split chosen from the shape and with no split.  Device-side
+    normal inputs (values do not change the work); K+V bytes / time is reported
+    next to TFLOP/s because these shapes are bound by reading K and V."""
+    import torch
+    from tiled_exact_attention_bf16_amd import attention as FA
+    from tiled_exact_attention_bf16_amd import workload as W
+    B, H, D, LK = 4, 16, 128, 16384
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k = torch.randn((B, LK, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, LK, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    res = {}
+    for lq in (1, 16, 128):
+        q = torch.randn((B, lq, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, lq), dtype=torch.float32, device="cuda")
+        flop = W.fwd_flops([lq] * B, [LK] * B, H, D, True)
+        kv_bytes = 2 * B * LK * H * D * 2
+        row = {}
+        for label, splits in (("auto_split", -1), ("no_split", 1)):
+            t = FA.Tuning(key_splits=splits)
+            ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+            fn = lambda: FA.fwd(q, k, v, 1.0 / D ** 0.5, True, tuning=t, out=o, lse=lse, workspace=ws)
+            for _ in range(warmup):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            row[label] = {"median_ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                          "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}
+        res[f"B{B} H{H} d{D} Lq{lq} Lk{LK} causal"] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +315,7 @@ def main():
     }
     if args.all_configs:
         out["configs"] = time_all_configs(det)
+        out["decode"] = time_decode()
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(inp)

@@ -109,11 +109,20 @@ typedef struct fa_fwd_tuning {
    * SIMD owning two 32-row blocks, each K/V fragment read once for both; 256-row
    * workgroups).  0 or negative = default. */
   int32_t rows_per_wave;
+  /* Split of each sequence's keys into this many contiguous chunks, each handled
+   * by its own workgroups (128-row query tiles); every chunk writes a partial O
+   * (fp32) and LSE to the workspace and a merge pass combines them:
+   * LSE = ln sum_c e^LSE_c, O = sum_c e^(LSE_c - LSE) O_c.  For short query
+   * sequences against long key sequences (generation with a cache), where the
+   * query tiles alone cannot fill the GPU.  1 = no split; 2..64 = that many;
+   * 0 or negative = chosen from the shape. */
+  int32_t key_splits;
 } fa_fwd_tuning;
 
-/* Bytes of device workspace fa_fwd needs for `a` (0 for fixed length; variable
- * length needs room for the longest-first work list). */
-fa_status fa_fwd_workspace_size(const fa_fwd_args* a, size_t* bytes);
+/* Bytes of device workspace fa_fwd needs for `a` and `tuning` (NULL = defaults):
+ * room for the longest-first work list of variable-length batches and for the
+ * partial results of a key split; 0 when neither is used. */
+fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tuning, size_t* bytes);
 
 /* Forward pass: writes O and LSE.  `workspace` (device, 256-byte aligned, at least
  * fa_fwd_workspace_size bytes, contents ignored on entry) may be NULL when that

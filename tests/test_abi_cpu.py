@@ -48,9 +48,10 @@ def fwd_args(b=2, s=256, h=4, d=128, causal=0, scale=0.088):
     return a
 
 
-def ws_size(a):
+def ws_size(a, tuning=None):
     n = ctypes.c_size_t(123)
-    st = L.lib().fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    t = tuning if tuning is not None else L.FwdTuning(-1, -1, -1, -1, -1)
+    st = L.lib().fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(t), ctypes.byref(n))
     return st, n.value
 
 
@@ -121,12 +122,14 @@ def varlen_args(n_seq=32, total=131072, max_len=16384, causal=1, h=16, d=128):
 
 def test_varlen_workspace_and_checks():
     a = varlen_args()
-    st, n = ws_size(a)
+    st, n = ws_size(a)                                  # default: 256-row work items
     assert st == L.FA_OK
-    items = (131072 + 127) // 128 + 32
-    assert n >= 4 * (1 + 2 * items) and n % 256 == 0
+    assert n >= 4 * (1 + 2 * ((131072 + 255) // 256 + 32)) and n % 256 == 0
+    t1 = L.FwdTuning(-1, -1, 1)
+    st, n1 = ws_size(a, t1)                             # 128-row work items: a longer list
+    assert st == L.FA_OK and n1 >= 4 * (1 + 2 * ((131072 + 127) // 128 + 32)) and n1 % 256 == 0
     assert fwd_status(a, ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
-    assert fwd_status(a, L.FwdTuning(-1, -1, 1), ws=P, ws_bytes=n - 256) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert fwd_status(a, t1, ws=P, ws_bytes=n1 - 256) == L.FA_ERR_WORKSPACE_TOO_SMALL
     assert fwd_status(a, ws=P + 16, ws_bytes=n) == L.FA_ERR_INVALID_ARGUMENT  # workspace alignment
     a.cu_seqlens_k = P + 0x6000000        # separate key offsets under the causal mask (bottom-right)
     assert ws_size(a)[0] == L.FA_OK
@@ -173,6 +176,22 @@ def test_backward_workspace_sizes():
     assert n_atomic >= rows * 128 * 4 + rows * 4          # fp32 dQ accumulator + row terms
     st, n_det = bwd_ws(bwd_args(det=1))
     assert st == L.FA_OK and rows * 4 <= n_det < n_atomic  # no accumulator in deterministic mode
+
+
+def test_key_split_workspace_and_validation():
+    a = fwd_args(b=2, s=256, h=4, d=128)
+    a.seqlen_q, a.seqlen_k = 8, 16384
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, -1, 1)) == (L.FA_OK, 0)          # split off: no workspace
+    st, n = ws_size(a, L.FwdTuning(-1, -1, -1, -1, 4))
+    rows = 4 * 4 * 2 * 8                                                   # splits * heads * total_q
+    assert st == L.FA_OK and n >= rows * 4 + rows * 128 * 4 and n % 256 == 0
+    st, n_auto = ws_size(a)                                                # 8 work items: split chosen
+    assert st == L.FA_OK and n_auto > 0
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, -1, 65))[0] == L.FA_ERR_UNSUPPORTED
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, 64, 2))[0] == L.FA_ERR_UNSUPPORTED
+    assert fwd_status(a, L.FwdTuning(-1, -1, -1, -1, 4), ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    big = fwd_args()                                                       # many work items: no split
+    assert ws_size(big) == (L.FA_OK, 0)
 
 
 def test_causal_with_unequal_lengths_is_accepted():

@@ -66,6 +66,35 @@ def test_causal_unequal_lengths(lq, lk, d, rpw):
     check_heads(inp, o, lse, [(b, h) for b in range(2) for h in range(2)], tag=f"causal{lq}x{lk}d{d}w{rpw}")
 
 
+# key splits: short query sequences against long key sequences (generation with a
+# cache); each chunk's partial O and LSE are merged by LSE weights
+@pytest.mark.parametrize("splits", [-1, 1, 3, 8])
+@pytest.mark.parametrize("b,lq,lk,h,d,causal", [(4, 1, 8192, 8, 128, False), (4, 1, 8192, 8, 128, True),
+                                               (2, 7, 5000, 4, 64, True), (1, 128, 16384, 4, 128, True),
+                                               (2, 33, 3000, 4, 128, False), (1, 300, 4096, 2, 128, True)])
+def test_key_splits(b, lq, lk, h, d, causal, splits):
+    inp = I.random_inputs(500 + lq + lk, b, lq, h, d, causal, seqlen_k=lk)
+    say(f"case split={splits} b={b} lq={lq} lk={lk} h={h} d={d} causal={causal}")
+    o, lse = run_fwd(inp, FA.Tuning(key_splits=splits))
+    pairs = [(0, 0), (b - 1, h - 1)]
+    check_heads(inp, o, lse, pairs, tag=f"split{splits} {b}x{lq}x{lk}x{h}d{d}c{int(causal)}")
+
+
+@pytest.mark.parametrize("splits", [-1, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_splits_varlen_separate_key_lengths(causal, splits):
+    q_lens = [1, 0, 5, 64, 130, 1, 17]
+    k_lens = [3000, 7, 4100, 64, 2000, 0, 9000]
+    inp = I.random_varlen_qk_inputs(77, q_lens, k_lens, heads=2, head_dim=128, causal=causal)
+    say(f"case varlen q/k lengths split={splits} causal={causal}")
+    q, k, v, _, cu = upload(inp)
+    cu_k = torch.from_numpy(inp.cu_seqlens_k).cuda()
+    o, lse = FA.fwd(q, k, v, inp.scale, causal, cu_seqlens_q=cu, cu_seqlens_k=cu_k, max_seqlen_q=inp.max_seqlen(),
+                    max_seqlen_k=inp.max_seqlen_k(), tuning=FA.Tuning(key_splits=splits))
+    torch.cuda.synchronize()
+    check_heads(inp, o, lse, [(bb, hh) for bb in range(len(q_lens)) for hh in range(2)], tag=f"varlenqk split{splits}")
+
+
 @pytest.mark.parametrize("variant", [(0, 8, 1, 32), (0, 8, 2, 32), (2, 8, 2, 32), (4, 8, 2, 32), (2, 8, 1, 32),
                                      (0, 0, 2, 32), (0, 0, 1, 32), (0, 8, 2, 64), (2, 8, 2, 64), (4, 8, 2, 64),
                                      (0, 0, 2, 64)])

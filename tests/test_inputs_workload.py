@@ -59,6 +59,10 @@ def test_causal_pair_count():
         brute = sum(i + 1 for i in range(n)) if n < 10000 else None
         assert W.visible_pairs(n, n, True) == brute
     assert W.visible_pairs(8192, 8192, True) * 2 - 8192 == 8192 * 8192
+    # unequal lengths under the causal mask: brute force over the bottom-right rule
+    for lq, lk in ((1, 9), (9, 1), (5, 12), (12, 5), (7, 7), (3, 1000)):
+        brute = sum(1 for i in range(lq) for j in range(lk) if j <= i + lk - lq)
+        assert W.visible_pairs(lq, lk, True) == brute
     # the headline shape: B=2, H=16, S=8192, d=128 causal
     assert W.fwd_flops([8192] * 2, [8192] * 2, 16, 128, True) == 4 * 128 * 16 * 2 * 8192 * 8193 // 2
     assert math.isclose(W.fwd_flops([8192] * 2, [8192] * 2, 16, 128, True), 5.498e11, rel_tol=1e-3)

@@ -51,7 +51,7 @@ class FwdArgs(ctypes.Structure):
 
 class FwdTuning(ctypes.Structure):
     _fields_ = [("exp2_poly_per16", c_int32), ("rescale_threshold_log2", c_int32),
-                ("q_tiles_per_workgroup", c_int32), ("rows_per_wave", c_int32)]
+                ("q_tiles_per_workgroup", c_int32), ("rows_per_wave", c_int32), ("key_splits", c_int32)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -72,7 +72,7 @@ _lib = None
 
 # name -> (restype, argtypes) for every entry point of include/fa_gfx950.h
 SIGNATURES = {
-    "fa_fwd_workspace_size": (c_int32, [POINTER(FwdArgs), POINTER(c_size_t)]),
+    "fa_fwd_workspace_size": (c_int32, [POINTER(FwdArgs), POINTER(FwdTuning), POINTER(c_size_t)]),
     "fa_fwd": (c_int32, [POINTER(FwdArgs), POINTER(FwdTuning), c_void_p, c_size_t, c_void_p]),
     "fa_fwd_build_schedule": (c_int32, [POINTER(FwdArgs), POINTER(FwdTuning), c_void_p, c_size_t, c_void_p]),
     "fa_fwd_tile_rows": (c_int32, [POINTER(FwdTuning)]),

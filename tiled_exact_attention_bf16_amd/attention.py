@@ -18,15 +18,17 @@ from . import _lib as L
 @dataclass
 class Tuning:
     """Forward variant: FMA-exp2 share (of 16), lazy threshold (log2 units), query tiles per
-    workgroup, query rows per wave (32 or 64).  -1 keeps the library default."""
+    workgroup, query rows per wave (32 or 64), key splits (1 = none).  -1 keeps the
+    library default."""
     exp2_poly_per16: int = -1
     rescale_threshold_log2: int = -1
     q_tiles_per_workgroup: int = -1
     rows_per_wave: int = -1
+    key_splits: int = -1
 
     def c(self):
         return L.FwdTuning(self.exp2_poly_per16, self.rescale_threshold_log2, self.q_tiles_per_workgroup,
-                           self.rows_per_wave)
+                           self.rows_per_wave, self.key_splits)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -97,11 +99,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Option
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     lib = L.lib()
+    t = (tuning or Tuning()).c()
     need = ctypes.c_size_t(0)
-    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_fwd_workspace_size")
+    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(t), ctypes.byref(need)), "fa_fwd_workspace_size")
     if need.value > 0 and (workspace is None or workspace.numel() < need.value):
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    t = (tuning or Tuning()).c()
     L.check(lib.fa_fwd(ctypes.byref(a), ctypes.byref(t), _ptr(workspace) if need.value else None,
                        need.value, _stream(stream)), "fa_fwd")
     return out, lse
@@ -113,10 +115,10 @@ def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[T
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, k, o, lse, 1.0, causal, cu_seqlens, None, max_seqlen, None)
     lib = L.lib()
-    need = ctypes.c_size_t(0)
-    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)), "fa_fwd_workspace_size")
-    ws = torch.zeros(max(need.value, 256), dtype=torch.uint8, device=q.device)
     t = (tuning or Tuning()).c()
+    need = ctypes.c_size_t(0)
+    L.check(lib.fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(t), ctypes.byref(need)), "fa_fwd_workspace_size")
+    ws = torch.zeros(max(need.value, 256), dtype=torch.uint8, device=q.device)
     L.check(lib.fa_fwd_build_schedule(ctypes.byref(a), ctypes.byref(t), _ptr(ws), ws.numel(), _stream(stream)),
             "fa_fwd_build_schedule")
     words = ws.view(torch.int32).cpu()

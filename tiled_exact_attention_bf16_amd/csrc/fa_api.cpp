@@ -3,6 +3,7 @@
 // rejected call leaves no work on the stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -88,15 +89,20 @@ fa_status check_tensor(const void* ptr, const int64_t st[3], const Shape& s, int
 int fwd_max_items(const Shape& s, int tile_rows) { return (s.total_q + tile_rows - 1) / tile_rows + s.batch; }
 
 struct FwdChoice {
-  int poly, tau, qt, rpw;
+  int poly, tau, qt, rpw, splits;  // splits <= 0: chosen from the shape
 };
+
+constexpr int kMaxKeySplits = 64;
 
 fa_status pick_tuning(const fa_fwd_tuning* t, FwdChoice* c) {
   c->poly = 0;
   c->tau = 8;
   c->qt = 2;
   c->rpw = 32;
+  c->splits = 0;
   if (t == nullptr) return FA_OK;
+  if (t->key_splits > kMaxKeySplits) return FA_ERR_UNSUPPORTED;
+  c->splits = t->key_splits > 0 ? t->key_splits : 0;
   if (t->exp2_poly_per16 >= 0) c->poly = t->exp2_poly_per16;
   if (t->rescale_threshold_log2 >= 0) c->tau = t->rescale_threshold_log2;
   if (t->q_tiles_per_workgroup >= 0) c->qt = t->q_tiles_per_workgroup;
@@ -104,6 +110,7 @@ fa_status pick_tuning(const fa_fwd_tuning* t, FwdChoice* c) {
   if (c->qt != 1 && c->qt != 2) return FA_ERR_UNSUPPORTED;
   if (c->rpw != 32 && c->rpw != 64) return FA_ERR_UNSUPPORTED;
   if (c->rpw == 64 && c->qt != 2) return FA_ERR_UNSUPPORTED;
+  if (c->splits > 1 && c->rpw == 64) return FA_ERR_UNSUPPORTED;  // the split path runs 128-row tiles
   if (c->tau == 8 && (c->poly == 0 || c->poly == 2 || c->poly == 4)) return FA_OK;
   if (c->tau == 0 && c->poly == 0) return FA_OK;
   return FA_ERR_UNSUPPORTED;
@@ -123,9 +130,38 @@ fa_status check_fwd(const fa_fwd_args* a, Shape* s) {
   return FA_OK;
 }
 
-size_t fwd_ws_bytes(const Shape& s, int tile_rows) {
-  if (!s.varlen) return 0;
-  return round_up(sizeof(int32_t) * (1 + 2 * (size_t)fwd_max_items(s, tile_rows)));
+// Key chunks for the split forward: more workgroups when the query tiles alone
+// (at 128 rows) leave the GPU short of work and every chunk still spans at least
+// 16 key tiles of 64.
+int fwd_key_splits(const Shape& s, const FwdChoice& c) {
+  if (c.splits > 0) return c.splits;
+  if (c.rpw == 64) return 1;
+  const int64_t items = (int64_t)(s.varlen ? fwd_max_items(s, fa::kFwdTileRows)
+                                           : (s.max_q + fa::kFwdTileRows - 1) / fa::kFwdTileRows * s.batch) *
+                        s.heads;
+  const int key_tiles = (s.max_k + fa::kFwdBlockN - 1) / fa::kFwdBlockN;
+  if (items >= 512 || key_tiles < 32) return 1;
+  const int want = (int)((1024 + items - 1) / items);
+  return std::max(1, std::min({want, key_tiles / 16, kMaxKeySplits}));
+}
+
+// Forward workspace: [work list (variable length)] [partial LSE] [partial O]
+struct FwdWs {
+  size_t lse_off, o_off, total;
+};
+
+FwdWs fwd_ws_layout(const Shape& s, int tile_rows, int splits) {
+  FwdWs w{};
+  size_t off = s.varlen ? round_up(sizeof(int32_t) * (1 + 2 * (size_t)fwd_max_items(s, tile_rows))) : 0;
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * s.heads * s.total_q;
+    w.lse_off = off;
+    off += round_up(rows * sizeof(float));
+    w.o_off = off;
+    off += round_up(rows * s.d * sizeof(float));
+  }
+  w.total = off;
+  return w;
 }
 
 fa::FwdParams make_fwd_params(const fa_fwd_args* a, const Shape& s) {
@@ -148,6 +184,7 @@ fa::FwdParams make_fwd_params(const fa_fwd_args* a, const Shape& s) {
   p.total_q = s.total_q;
   p.scale = a->softmax_scale;
   p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+  p.n_split = 1;
   return p;
 }
 
@@ -171,16 +208,18 @@ const char* fa_version(void) { return "fa_gfx950 0.1"; }
 int32_t fa_fwd_tile_rows(const fa_fwd_tuning* tuning) {
   FwdChoice c;
   if (pick_tuning(tuning, &c) != FA_OK) return 0;
-  return fa::kFwdTileRows * c.qt;
+  return c.splits > 1 ? fa::kFwdTileRows : fa::kFwdTileRows * c.qt;
 }
 
-fa_status fa_fwd_workspace_size(const fa_fwd_args* a, size_t* bytes) {
+fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tuning, size_t* bytes) {
   if (bytes == nullptr) return FA_ERR_INVALID_ARGUMENT;
   Shape s;
   fa_status st = check_fwd(a, &s);
   if (st != FA_OK) return st;
-  // the largest work list over the compiled tile heights
-  *bytes = fwd_ws_bytes(s, fa::kFwdTileRows);
+  FwdChoice c;
+  if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
+  const int splits = fwd_key_splits(s, c);
+  *bytes = fwd_ws_layout(s, splits > 1 ? fa::kFwdTileRows : fa::kFwdTileRows * c.qt, splits).total;
   return FA_OK;
 }
 
@@ -192,11 +231,12 @@ fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tunin
   FwdChoice c;
   if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
   if (!s.varlen) return FA_ERR_INVALID_ARGUMENT;
-  const size_t need = fwd_ws_bytes(s, fa::kFwdTileRows * c.qt);
+  const int tile_rows = fwd_key_splits(s, c) > 1 ? fa::kFwdTileRows : fa::kFwdTileRows * c.qt;
+  const size_t need = fwd_ws_layout(s, tile_rows, 1).total;
   if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
   if ((uintptr_t)workspace % kAlign) return FA_ERR_INVALID_ARGUMENT;
-  hipError_t e = fa::launch_fwd_schedule(s.cu_q, s.cu_k, s.batch, fa::kFwdTileRows * c.qt, fa::kFwdBlockN,
-                                         a->causal != 0, (int32_t*)workspace, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd_schedule(s.cu_q, s.cu_k, s.batch, tile_rows, fa::kFwdBlockN, a->causal != 0,
+                                         (int32_t*)workspace, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -207,17 +247,24 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
   if (st != FA_OK) return st;
   FwdChoice c;
   if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
+  const int splits = fwd_key_splits(s, c);
+  if (splits > 1) c.qt = 1;  // the split path runs 128-row tiles
   const int tile_rows = fa::kFwdTileRows * c.qt;
-  const size_t need = fwd_ws_bytes(s, tile_rows);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && (uintptr_t)workspace % kAlign) return FA_ERR_INVALID_ARGUMENT;
-  if ((int64_t)fwd_max_items(s, tile_rows) * s.heads > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  const FwdWs ws = fwd_ws_layout(s, tile_rows, splits);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws.total > 0 && (uintptr_t)workspace % kAlign) return FA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)fwd_max_items(s, tile_rows) * s.heads * splits > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (s.batch == 0 || s.total_q == 0) return FA_OK;
 
   fa::FwdParams p = make_fwd_params(a, s);
   p.n_qtiles = s.varlen ? 0 : (s.max_q + tile_rows - 1) / tile_rows;
   p.sched = (const int32_t*)workspace;
-  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, c.rpw};
+  if (splits > 1) {
+    p.n_split = splits;
+    p.part_lse = (float*)((char*)workspace + ws.lse_off);
+    p.part_o = (float*)((char*)workspace + ws.o_off);
+  }
+  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, c.rpw, splits};
   hipStream_t strm = (hipStream_t)stream;
   if (s.varlen) {
     hipError_t e = fa::launch_fwd_schedule(s.cu_q, s.cu_k, s.batch, tile_rows, fa::kFwdBlockN, cfg.causal,

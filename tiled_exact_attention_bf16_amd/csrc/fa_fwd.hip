@@ -32,7 +32,7 @@
 
 namespace fa {
 
-template <int D, int NQT, bool CAUSAL, bool VARLEN, int POLY, int TAU>
+template <int D, int NQT, bool CAUSAL, bool VARLEN, int POLY, int TAU, bool SPLIT = false>
 __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   constexpr int BN = kFwdBlockN;
   constexpr int NW = 4 * NQT;
@@ -58,18 +58,20 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5;
 
-  // ---- work item ----
+  // ---- work item (and key chunk when the keys are split) ----
+  const int chunk = SPLIT ? (int)(blockIdx.x % (unsigned)p.n_split) : 0;
+  const int wid = SPLIT ? (int)(blockIdx.x / (unsigned)p.n_split) : (int)blockIdx.x;
   int b, h, qtile;
   if constexpr (VARLEN) {
-    const int item = blockIdx.x / p.heads;
-    h = blockIdx.x - item * p.heads;
+    const int item = wid / p.heads;
+    h = wid - item * p.heads;
     if (item >= p.sched[0]) return;
     b = p.sched[1 + 2 * item];
     qtile = p.sched[2 + 2 * item];
   } else {
     const int bh_count = p.batch * p.heads;
-    const int t = blockIdx.x / bh_count;
-    const int bh = blockIdx.x - t * bh_count;
+    const int t = wid / bh_count;
+    const int bh = wid - t * bh_count;
     qtile = CAUSAL ? (p.n_qtiles - 1 - t) : t;  // longest first under the causal mask
     b = bh / p.heads;
     h = bh - b * p.heads;
@@ -94,6 +96,21 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   }
   const int wg_q0 = qtile * WG_ROWS;
   if (wg_q0 >= Lq) return;
+  // causal: row i sees keys j <= i + coff (the mask's diagonal ends at the last query
+  // and the last key; coff = 0 for equal lengths)
+  int coff = Lk - Lq;
+  int64_t row_base = 0;  // this sequence's first row among all query rows (split output)
+  if constexpr (SPLIT) {
+    // chunk `chunk` of the key tiles: shift K/V to its first key and shrink Lk
+    row_base = VARLEN ? (int64_t)p.cu_q[b] : (int64_t)b * Lq;
+    const int tiles = (Lk + kFwdBlockN - 1) / kFwdBlockN;
+    const int per = (tiles + p.n_split - 1) / p.n_split;
+    const int kbase = min(chunk * per, tiles) * kFwdBlockN;
+    koff += (int64_t)kbase * p.k_ss;
+    voff += (int64_t)kbase * p.v_ss;
+    Lk = max(0, min(Lk - kbase, per * kFwdBlockN));
+    coff -= kbase;
+  }
 
   const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), k_ss2 = (uint32_t)(p.k_ss * 2);
   const uint32_t v_ss2 = (uint32_t)(p.v_ss * 2), o_ss2 = (uint32_t)(p.o_ss * 2);
@@ -110,9 +127,6 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   for (int ds = 0; ds < NDS; ++ds) qreg[ds] = buf_load16(rq, (uint32_t)my_row * q_ss2 + (2 * ds + hl) * 16);
 
   int kv_end = Lk;
-  // causal: row i sees keys j <= i + coff (the mask's diagonal ends at the last query
-  // and the last key; coff = 0 for equal lengths)
-  const int coff = Lk - Lq;
   if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
   const int n_tiles = (kv_end + BN - 1) / BN;
 
@@ -157,8 +171,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
 
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
   // last tile; it then only helps stage K/V and keeps the barriers.
-  int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = (q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
+  int n_mine = q0 < Lq ? n_tiles : 0;  // a wave whose rows are all past the end only helps stage K/V
+  if constexpr (CAUSAL) n_mine = (q0 >= Lq || q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
 
   // ---- one pipelined step j: S(j) = K(j) Q^T runs on the matrix cores while the
   // weights of tile j-1 are exponentiated; then O^T += V(j-1)^T P(j-1)^T runs
@@ -351,19 +365,33 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   const float lt = half_swap_sum(lsum);
   const float ltr = half_swap_sum(lsum_r);
   const float inv = ltr > 0.0f ? 1.0f / ltr : 0.0f;
+  float lse = -INFINITY;
+  if (lt > 0.0f) lse = (m_used * c + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+  if constexpr (SPLIT) {
+    // this chunk's normalised partial O (fp32) and LSE; rows past the end are dropped
+    const int64_t slot = ((int64_t)chunk * p.heads + h) * p.total_q + row_base;
+    const rsrc_t rpo = make_rsrc(p.part_o + slot * D, (uint32_t)Lq * D * 4);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * hl;
-      const u32x2 w = {pack_bf16(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
-                       pack_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
-      buf_store8(ro, (uint32_t)my_row * o_ss2 + d * 2, w);
-    }
-  if (hl == 0 && my_row < Lq) {
-    float lse = -INFINITY;
-    if (lt > 0.0f) lse = (m_used * c + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
-    p.lse[lseoff + my_row] = lse;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * db + 8 * q4 + 4 * hl;
+        buf_store16(rpo, ((uint32_t)my_row * D + d) * 4,
+                    u32x4{__float_as_uint(oacc[db][4 * q4 + 0] * inv), __float_as_uint(oacc[db][4 * q4 + 1] * inv),
+                          __float_as_uint(oacc[db][4 * q4 + 2] * inv), __float_as_uint(oacc[db][4 * q4 + 3] * inv)});
+      }
+    if (hl == 0 && my_row < Lq) p.part_lse[slot + my_row] = lse;
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * db + 8 * q4 + 4 * hl;
+        const u32x2 w = {pack_bf16(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
+                         pack_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
+        buf_store8(ro, (uint32_t)my_row * o_ss2 + d * 2, w);
+      }
+    if (hl == 0 && my_row < Lq) p.lse[lseoff + my_row] = lse;
   }
 }
 
@@ -733,6 +761,50 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
   finish(B, row_b);
 }
 
+// ---- merge of the key chunks' partial results ----
+// One thread per (head, query row, 4 columns of O): LSE = m + ln sum_c e^(LSE_c - m)
+// with m = max_c LSE_c, and O = sum_c e^(LSE_c - LSE) O_c, in chunk order.  Chunks
+// where the row saw no key carry LSE_c = -inf and weigh nothing; a row that saw no
+// key at all gets O = 0, LSE = -inf.
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.heads * p.total_q;
+  if (idx >= rows * (D / 4)) return;
+  const int64_t r = idx / (D / 4);
+  const int d = (int)(idx - r * (D / 4)) * 4;
+  const int h = (int)(r / p.total_q);
+  const int rowg = (int)(r - (int64_t)h * p.total_q);
+  const int64_t stride = (int64_t)p.heads * p.total_q;  // between chunks
+  float m = -INFINITY;
+  for (int c = 0; c < p.n_split; ++c) m = fmaxf(m, p.part_lse[c * stride + r]);
+  float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f, wsum = 0.0f;
+  if (m != -INFINITY) {
+    for (int c = 0; c < p.n_split; ++c) {
+      const float lc = p.part_lse[c * stride + r];
+      const float w = __expf(lc - m);  // 0 for an empty chunk
+      const f32x4 oc = *(const f32x4*)(p.part_o + (c * stride + r) * D + d);
+      o0 = __builtin_fmaf(w, oc[0], o0);
+      o1 = __builtin_fmaf(w, oc[1], o1);
+      o2 = __builtin_fmaf(w, oc[2], o2);
+      o3 = __builtin_fmaf(w, oc[3], o3);
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  int64_t ooff, lidx;
+  if constexpr (VARLEN) {
+    ooff = (int64_t)rowg * p.o_ss + (int64_t)h * p.o_sh;
+    lidx = (int64_t)h * p.total_q + rowg;
+  } else {
+    const int b = rowg / p.seqlen_q, i = rowg - b * p.seqlen_q;
+    ooff = (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
+    lidx = ((int64_t)b * p.heads + h) * p.seqlen_q + i;
+  }
+  *(u32x2*)((uint16_t*)p.o + ooff + d) = u32x2{pack_bf16(o0 * inv, o1 * inv), pack_bf16(o2 * inv, o3 * inv)};
+  if (d == 0) p.lse[lidx] = wsum > 0.0f ? m + __logf(wsum) : -INFINITY;
+}
+
 // ---- longest-first work list for packed variable-length batches ----
 // One workgroup: histogram of item costs (key tiles visited), exclusive scan from
 // the most expensive bin down, scatter.  Items of equal cost may land in any order.
@@ -790,6 +862,18 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream, int max_ite
   const int items = VARLEN ? max_items : p.n_qtiles * p.batch;
   const unsigned grid = (unsigned)items * (unsigned)p.heads;
   if (grid == 0) return hipSuccess;
+  if constexpr (NQT == 1) {
+    if (p.n_split > 1) {
+      hipLaunchKernelGGL((fwd_kernel<D, 1, CAUSAL, VARLEN, POLY, TAU, true>), dim3(grid * (unsigned)p.n_split),
+                         dim3(256), 0, stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t threads = (int64_t)p.heads * p.total_q * (D / 4);
+      hipLaunchKernelGGL((fwd_merge_kernel<D, VARLEN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
   if constexpr (NQT == 2) {
     if (rows_per_wave == 64) {
       hipLaunchKernelGGL((fwd64_kernel<D, CAUSAL, VARLEN, POLY, TAU>), dim3(grid), dim3(256), 0, stream, p);

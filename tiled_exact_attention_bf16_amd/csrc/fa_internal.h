@@ -32,6 +32,13 @@ struct FwdParams {
   const int32_t* sched;  // variable length: {count, (seq, tile) pairs...}
   float scale;         // softmax scale
   float scale_log2;    // softmax scale * log2(e)
+  // key split (n_split > 1): chunk c of every sequence's keys writes its partial
+  // LSE to part_lse[(c*heads + h)*total_q + row] and its partial O (fp32) to
+  // part_o[((c*heads + h)*total_q + row)*D]; row counts through the packed or
+  // batched query rows (b*seqlen_q + i for fixed length)
+  int n_split;
+  float* part_lse;
+  float* part_o;
 };
 
 struct FwdConfig {
@@ -42,6 +49,7 @@ struct FwdConfig {
   int poly_per16;   // 0, 2, 4
   int tau;          // 8 or 0
   int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd64_kernel, q_tiles == 2)
+  int key_splits;     // 1, or > 1 for the split forward (q_tiles == 1, 32 rows per wave) + merge
 };
 
 // Returns hipSuccess or the launch error.  Grid size is derived from p and cfg.

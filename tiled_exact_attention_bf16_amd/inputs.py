@@ -36,6 +36,7 @@ __all__ = [
     "make_inputs",
     "random_inputs",
     "random_varlen_inputs",
+    "random_varlen_qk_inputs",
 ]
 
 
@@ -115,7 +116,8 @@ class AttnInputs:
 
     Fixed length: q/k/v/do have shape [B, S, H, D] and cu_seqlens is None.
     Variable length: q/k/v/do have shape [T, H, D] (sequences packed along T) and
-    cu_seqlens is the int32 prefix sum of the lengths ([B+1], first entry 0).
+    cu_seqlens is the int32 prefix sum of the lengths ([B+1], first entry 0);
+    cu_seqlens_k, when given, holds the key/value offsets (else the same as q's).
     """
     name: str
     q: np.ndarray
@@ -126,6 +128,7 @@ class AttnInputs:
     do: Optional[np.ndarray] = None
     cu_seqlens: Optional[np.ndarray] = None
     seed: int = 0
+    cu_seqlens_k: Optional[np.ndarray] = None
 
     @property
     def varlen(self) -> bool:
@@ -151,11 +154,20 @@ class AttnInputs:
     def max_seqlen(self) -> int:
         return int(self.seqlens().max()) if self.batch > 0 else 0
 
+    def seqlens_k(self) -> np.ndarray:
+        if self.varlen:
+            return np.diff(self.cu_seqlens if self.cu_seqlens_k is None else self.cu_seqlens_k).astype(np.int64)
+        return np.full(self.k.shape[0], self.k.shape[1], dtype=np.int64)
+
+    def max_seqlen_k(self) -> int:
+        return int(self.seqlens_k().max()) if self.batch > 0 else 0
+
     def sequence(self, b: int, name: str = "q") -> np.ndarray:
         """bf16 bits of one sequence of one tensor, shape [L, H, D]."""
         t = getattr(self, name)
         if self.varlen:
-            s, e = int(self.cu_seqlens[b]), int(self.cu_seqlens[b + 1])
+            cu = self.cu_seqlens_k if (name in ("k", "v") and self.cu_seqlens_k is not None) else self.cu_seqlens
+            s, e = int(cu[b]), int(cu[b + 1])
             return t[s:e]
         return t[b]
 
@@ -198,6 +210,23 @@ def random_varlen_inputs(seed: int, lengths, heads: int, head_dim: int, causal: 
 
 # The five workloads and the headline forward shape.  Sizes follow the method's
 # long-sequence regime; values are synthetic normals.
+def random_varlen_qk_inputs(seed: int, q_lengths, k_lengths, heads: int, head_dim: int, causal: bool,
+                            name: str = "varlen_qk") -> AttnInputs:
+    """Packed problem with separate query and key lengths per sequence."""
+    rng = np.random.default_rng(seed)
+    q_lengths = np.asarray(q_lengths, dtype=np.int64)
+    k_lengths = np.asarray(k_lengths, dtype=np.int64)
+    cu_q = np.zeros(len(q_lengths) + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(q_lengths)
+    cu_k = np.zeros(len(k_lengths) + 1, dtype=np.int32)
+    cu_k[1:] = np.cumsum(k_lengths)
+    q = _draw_bf16(rng, (int(cu_q[-1]), heads, head_dim), 1.0)
+    k = _draw_bf16(rng, (int(cu_k[-1]), heads, head_dim), 1.0)
+    v = _draw_bf16(rng, (int(cu_k[-1]), heads, head_dim), 1.0)
+    return AttnInputs(name=name, q=q, k=k, v=v, scale=_fp32_scale(head_dim), causal=causal, cu_seqlens=cu_q,
+                      seed=seed, cu_seqlens_k=cu_k)
+
+
 CONFIGS = {
     "c1": dict(seed=1, batch=1, seqlen=256, heads=2, head_dim=64, causal=False),
     "c2": dict(seed=2, batch=4, seqlen=4096, heads=16, head_dim=128, causal=False),

@@ -22,12 +22,11 @@ def visible_pairs(seqlen_q: int, seqlen_k: int, causal: bool) -> int:
         return 0
     if not causal:
         return seqlen_q * seqlen_k
-    # key j visible to query i iff j <= i (top-left aligned)
+    # key j visible to query i iff j <= i + seqlen_k - seqlen_q (bottom-right aligned):
+    # the last n = min(seqlen_q, seqlen_k) queries see seqlen_k - n + 1 ... seqlen_k keys,
+    # the earlier queries (only when seqlen_q > seqlen_k) see none
     n = min(seqlen_q, seqlen_k)
-    pairs = n * (n + 1) // 2
-    if seqlen_q > seqlen_k:
-        pairs += (seqlen_q - seqlen_k) * seqlen_k
-    return pairs
+    return n * (seqlen_k - n) + n * (n + 1) // 2
 
 
 def total_pairs(seqlens_q: Sequence[int], seqlens_k: Sequence[int], heads: int, causal: bool) -> int:
