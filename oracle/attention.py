@@ -105,11 +105,14 @@ def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool)
 
 
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
-                  causal: bool) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                  causal: bool, o: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients (dQ, dK, dV) of one head's attention for the output gradient dO.
 
     O and LSE are recomputed here in fp64 from the inputs (never taken from a
-    GPU run), then P is rebuilt block by block from LSE.
+    GPU run), then P is rebuilt block by block from LSE.  ``o``, when given, is
+    the forward output as the backward receives it (e.g. rounded to bf16) and
+    enters only D_i = sum_d dO_id O_id, as it does in a backward that reads the
+    saved output; by default D uses the exact O.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -121,8 +124,8 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     dv = np.zeros_like(v)
     if lq == 0 or lk == 0:
         return dq, dk, dv
-    o, lse = head_forward(q, k, v, scale, causal)
-    dvec = (do * o).sum(axis=1)
+    o_exact, lse = head_forward(q, k, v, scale, causal)
+    dvec = (do * (o_exact if o is None else np.asarray(o, dtype=np.float64))).sum(axis=1)
     scale = float(scale)
     for b0 in range(0, lq, ROW_BLOCK):
         r = np.arange(b0, min(lq, b0 + ROW_BLOCK))

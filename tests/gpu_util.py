@@ -72,15 +72,23 @@ def oracle_fwd_head(inp: I.AttnInputs, b: int, h: int, rows=None):
     return OA.head_forward(q, k, v, inp.scale, inp.causal, rows=rows)
 
 
-def oracle_bwd_head(inp: I.AttnInputs, b: int, h: int):
+def oracle_bwd_head(inp: I.AttnInputs, b: int, h: int, o_bf16: bool = False):
+    """Oracle gradients; o_bf16: D_i from the oracle's own O rounded to bf16, i.e. the
+    forward output as a backward that reads the stored bf16 O receives it."""
     q, k, v, do = (head_slices(inp, b, h, t) for t in ("q", "k", "v", "do"))
-    return OA.head_backward(q, k, v, do, inp.scale, inp.causal)
+    o = None
+    if o_bf16:
+        o_exact, _ = OA.head_forward(q, k, v, inp.scale, inp.causal)
+        o = I.bf16_bits_to_f64(I.f32_to_bf16_bits(o_exact.astype(np.float32)))
+    return OA.head_backward(q, k, v, do, inp.scale, inp.causal, o=o)
 
 
-def gpu_head(t: torch.Tensor, inp: I.AttnInputs, b: int, h: int) -> np.ndarray:
-    """[L, D] slice of a GPU output tensor (same layout as the inputs), as float64 numpy."""
+def gpu_head(t: torch.Tensor, inp: I.AttnInputs, b: int, h: int, kind: str = "q") -> np.ndarray:
+    """[L, D] slice of a GPU output tensor (same layout as the inputs), as float64 numpy.
+    kind "k" slices key-shaped tensors (dK, dV) by the key offsets."""
     if inp.varlen:
-        s0, s1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        cu = inp.cu_seqlens_k if (kind == "k" and inp.cu_seqlens_k is not None) else inp.cu_seqlens
+        s0, s1 = int(cu[b]), int(cu[b + 1])
         x = t[s0:s1, h]
     else:
         x = t[b, :, h]

@@ -107,3 +107,24 @@ def test_bottom_right_causal_against_torch_autograd(lq, lk):
     assert np.all(dq[~seen] == 0.0)
     for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
         assert np.max(np.abs(mine - np.nan_to_num(ref.numpy()))) <= 1e-11
+
+
+def test_given_output_enters_only_through_d():
+    """The backward may be handed the forward output (rounded, as a kernel stores it):
+    with the exact output nothing changes; a perturbation of O changes D_i by
+    dD_i = dO_i . delta_i, which moves dQ_i by -scale * dD_i * sum_j P_ij k_j and dK_j
+    by -scale * sum_i P_ij dD_i q_i, and leaves dV unchanged."""
+    n, d = 40, 8
+    q, k, v, do = (_rand((n, d), s) for s in (80, 81, 82, 83))
+    base = A.head_backward(q, k, v, do, 0.4, True)
+    o, _ = A.head_forward(q, k, v, 0.4, True)
+    same = A.head_backward(q, k, v, do, 0.4, True, o=o)
+    for x, y in zip(base, same):
+        assert np.max(np.abs(x - y)) == 0.0
+    delta = _rand((n, d), 84) * 1e-3
+    dq2, dk2, dv2 = A.head_backward(q, k, v, do, 0.4, True, o=o + delta)
+    dd = (do * delta).sum(axis=1)                       # change of D_i
+    p = A.head_probabilities(q, k, 0.4, True)
+    assert np.max(np.abs(dv2 - base[2])) == 0.0
+    assert np.max(np.abs(dq2 - (base[0] - 0.4 * (p * dd[:, None]) @ k))) <= 1e-13
+    assert np.max(np.abs(dk2 - (base[1] - 0.4 * (p * dd[:, None]).T @ q))) <= 1e-13
