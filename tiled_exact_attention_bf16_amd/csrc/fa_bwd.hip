@@ -26,6 +26,8 @@
 // every matrix-core operation stays BF16.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -496,10 +498,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   constexpr int WG_ROWS = 32 * NW;
   constexpr int ROWB = D * 2;
   constexpr int TILE_BYTES = BN * ROWB;
-  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   constexpr int SLOTS = D / 8, NKB = BN / 32, NDS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  // K and V of the two stages as separate objects, so that the compiler can tell the
+  // buffers a tile reads from the ones the next tile's DMA loads fill
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
+  auto kbuf = [&](int st) { return (FA_LDS char*)(st ? k_lds1 : k_lds0); };
+  auto vbuf = [&](int st) { return (FA_LDS char*)(st ? v_lds1 : v_lds0); };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -555,13 +562,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int coff = Lk - Lq;  // causal: row i sees keys j <= i + coff
   if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
   const int n_tiles = (kv_end + BN - 1) / BN;
-  int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = (q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
+  int n_mine = q0 < Lq ? n_tiles : 0;  // a wave whose rows are all past the end only helps stage K/V
+  if constexpr (CAUSAL) n_mine = (q0 >= Lq || q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
 
   auto issue_tile = [&](int t, int stage) {
     const int k0 = t * BN;
-    FA_LDS char* kd = smem + stage * STAGE_BYTES;
-    FA_LDS char* vd = kd + TILE_BYTES;
+    FA_LDS char* kd = kbuf(stage);
+    FA_LDS char* vd = vbuf(stage);
 #pragma unroll
     for (int i = wave; i < TILE_BYTES / 1024; i += NW) {
       const int idx = i * 64 + lane;
@@ -572,37 +579,49 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // lane-constant LDS offsets within a tile: with the stage a compile-time constant
+  // every operand read is one register plus an immediate
   const int sw_row = slot_swizzle<D>(lane & 15);
   const int tr_r1 = 4 * hl + (i16 >> 2);
   const int sw_t1 = slot_swizzle<D>(tr_r1), sw_t2 = slot_swizzle<D>(tr_r1 + 8);
   const int tr_clo = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
   const int tr_half = (i16 & 1) * 8;
+  int off_r[NDS], off_t1[NDB], off_t2[NDB];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) off_r[ds] = (lane & 31) * ROWB + (((2 * ds + hl) ^ sw_row) << 4);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int cc = 4 * db + tr_clo;
+    off_t1[db] = tr_r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half;
+    off_t2[db] = (tr_r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half;
+  }
   const float c = p.scale_log2;
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  int t = 0;
-  for (; t < n_mine; ++t) {
-    const int stage = t & 1;
+  // one tile of 64 keys; MASK: the tile may hold keys this wave must not see
+  auto tile = [&](const int t, auto stage_c, auto mask_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
+    if (t + 1 < n_tiles) issue_tile(t + 1, STAGE ^ 1);
     const int k0 = t * BN;
-    const FA_LDS char* kt = smem + stage * STAGE_BYTES;
-    const FA_LDS char* vt = kt + TILE_BYTES;
-    bool need_mask = (k0 + BN > Lk);
-    if constexpr (CAUSAL) need_mask = need_mask || (k0 + BN - 1 > q0 + coff);
+    const FA_LDS char* kt = kbuf(STAGE);
+    const FA_LDS char* vt = vbuf(STAGE);
+    // key k0 + rel is hidden from this lane's row when rel >= lim
+    int lim = Lk;
+    if constexpr (CAUSAL) lim = min(lim, my_row + 1 + coff);
+    lim -= k0 + 4 * hl;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const int ro = (32 * kb + (lane & 31)) * ROWB + (((2 * ds + hl) ^ sw_row) << 4);
-        s = mfma_bf16(lds_read16(kt + ro), qreg[ds], s);
-        dp = mfma_bf16(lds_read16(vt + ro), doreg[ds], dp);
+        s = mfma_bf16(lds_read16(kt + 32 * kb * ROWB + off_r[ds]), qreg[ds], s);
+        dp = mfma_bf16(lds_read16(vt + 32 * kb * ROWB + off_r[ds]), doreg[ds], dp);
       }
       u32x4 dsh[2], dsl[2];
 #pragma unroll
@@ -615,12 +634,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           for (int u = 0; u < 2; ++u) {
             const int r = 8 * half + 2 * e + u;
             float pe = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
-            if (need_mask) {
-              const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-              bool hide = key >= Lk;
-              if constexpr (CAUSAL) hide = hide || key > my_row + coff;
-              pe = hide ? 0.0f : pe;
-            }
+            if constexpr (MASK) pe = (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) ? 0.0f : pe;
             dv2[u] = pe * __builtin_fmaf(dp[r], p.scale, -dvs);   // scale * P (dP - D)
           }
           hh[e] = pack_bf16(dv2[0], dv2[1]);
@@ -632,18 +646,40 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       // dQ^T += K^T dS'^T  (A = K^T through the transpose reads, 16-key groups)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int r1 = 32 * kb + 16 * half + tr_r1;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int cc = 4 * db + tr_clo;
-          const u32x2 lo = lds_read_tr16(kt + r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half);
-          const u32x2 hi = lds_read_tr16(kt + (r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half);
+          const int rb = (32 * kb + 16 * half) * ROWB;
+          const u32x2 lo = lds_read_tr16(kt + rb + off_t1[db]);
+          const u32x2 hi = lds_read_tr16(kt + rb + off_t2[db]);
           const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
           dqacc[db] = mfma_bf16(a, dsh[half], dqacc[db]);
           dqacc[db] = mfma_bf16(a, dsl[half], dqacc[db]);
         }
       }
     }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using MF = std::false_type;
+  using MT = std::true_type;
+  // tiles before t_plain need no mask for this wave's rows
+  int t_plain = Lk / BN;
+  if constexpr (CAUSAL) t_plain = min(t_plain, max(0, q0 + 1 + coff) / BN);
+  const int t_lim = min(n_mine, t_plain);
+  if (n_tiles > 0) issue_tile(0, 0);
+  int t = 0;
+  for (; t + 1 < t_lim; t += 2) {
+    tile(t, I0{}, MF{});
+    tile(t + 1, I1{}, MF{});
+  }
+  for (; t + 1 < n_mine; t += 2) {
+    tile(t, I0{}, MT{});
+    tile(t + 1, I1{}, MT{});
+  }
+  if (t < n_mine) {
+    tile(t, I0{}, MT{});
+    ++t;
   }
   for (; t < n_tiles; ++t) {
     wait_vmem();
