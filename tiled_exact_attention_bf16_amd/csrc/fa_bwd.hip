@@ -202,15 +202,20 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   // Deterministic mode needs no dS staging, which leaves room to double-buffer the
   // Q/dO stage; the atomic mode's single stage is refilled during its dQ part.
   constexpr int NSTAGE = DQ_ATOMIC ? 1 : 2;
-  constexpr int MAIN_BYTES = NSTAGE * STAGE + 2 * KT_BYTES + 2 * DS_BYTES;
-  constexpr int RED_BYTES = 4 * 64 * (2 * D / 2) * 4;  // 4 waves x 64 lanes x (dK,dV halves) fp32
-  constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
-  FA_LDS char* k_lds = smem + NSTAGE * STAGE;
-  FA_LDS char* v_lds = k_lds + KT_BYTES;
-  FA_LDS char* dsh_lds = v_lds + KT_BYTES;
-  FA_LDS char* dsl_lds = dsh_lds + DS_BYTES;
+  // Every buffer is its own object, so that the compiler can tell the stage a step
+  // reads from the one the next step's DMA loads fill (and does not make the reads
+  // wait for those loads).  The final dK/dV reduction reuses the K and V buffers.
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[NSTAGE == 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char k_lds_raw[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds_raw[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsh_raw[DQ_ATOMIC ? DS_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char dsl_raw[DQ_ATOMIC ? DS_BYTES : 16];
+  auto stage_buf = [&](int st) { return (FA_LDS char*)(st ? stage1 : stage0); };
+  FA_LDS char* k_lds = (FA_LDS char*)k_lds_raw;
+  FA_LDS char* v_lds = (FA_LDS char*)v_lds_raw;
+  FA_LDS char* dsh_lds = (FA_LDS char*)dsh_raw;
+  FA_LDS char* dsl_lds = (FA_LDS char*)dsl_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   const float c = p.scale_log2;
 
   auto issue_q = [&](int i, int stage) {
-    FA_LDS char* qt = smem + stage * STAGE;
+    FA_LDS char* qt = stage_buf(stage);
     FA_LDS char* dot = qt + QT_BYTES;
 #pragma unroll
     for (int j = wave; j < QT_BYTES / 1024; j += 8) {
@@ -313,11 +318,12 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
     issue_q(i_start, 0);
     load_terms(i_start);
   }
-  for (int it = 0; it < n_steps; ++it) {
+  // one step: the 64 query rows i_start + it; the stage is a compile-time constant
+  auto step = [&](const int it, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const int i = i_start + it;
     const int q0 = i * BM;
-    const int stage = NSTAGE == 2 ? (it & 1) : 0;
-    FA_LDS char* qt = smem + stage * STAGE;
+    FA_LDS char* qt = stage_buf(stage);
     FA_LDS char* dot = qt + QT_BYTES;
     FA_LDS float* lse_l = (FA_LDS float*)(dot + QT_BYTES);
     FA_LDS float* dvec_l = lse_l + BM;
@@ -445,39 +451,55 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
                                                           0, 0);
       }
     }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (NSTAGE == 2) {
+    int it = 0;
+    for (; it + 1 < n_steps; it += 2) {
+      step(it, I0{});
+      step(it + 1, I1{});
+    }
+    if (it < n_steps) step(it, I0{});
+  } else {
+    for (int it = 0; it < n_steps; ++it) step(it, I0{});
   }
 
   // ---- sum the two row-half partials of each key group, then store dK, dV ----
-  __syncthreads();
-  FA_LDS f32x4* red = (FA_LDS f32x4*)smem + kw * (64 * 2 * NDB * 4);
-  if (qh == 1) {
+  // One 32-column block of d per round through the (now free) K and V buffers:
+  // [key group][4 rows of 4][64 lanes] f32x4 each, dK in k_lds and dV in v_lds.
+  const int gb = p.grad_bf16 ? 2 : 4;
+  const rsrc_t rdk = make_rsrc((char*)p.dk + sq.dkoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dk_ss * gb) + D * gb : 0u);
+  const rsrc_t rdv = make_rsrc((char*)p.dv + sq.dvoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dv_ss * gb) + D * gb : 0u);
+  const uint32_t dk_row = (uint32_t)my_key * (uint32_t)(p.dk_ss * gb);
+  const uint32_t dv_row = (uint32_t)my_key * (uint32_t)(p.dv_ss * gb);
+  FA_LDS f32x4* red_k = (FA_LDS f32x4*)k_lds + kw * (4 * 64);
+  FA_LDS f32x4* red_v = (FA_LDS f32x4*)v_lds + kw * (4 * 64);
+  static_assert(4 * 4 * 64 * 16 <= KT_BYTES, "one reduction round must fit a K/V buffer");
+  wait_vmem();  // with no query step the K/V loads were never waited for
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db) {
+    __syncthreads();  // the buffers are free (main loop or the previous round done)
+    if (qh == 1) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        red[((2 * db) * 4 + r4) * 64 + lane] = f32x4{dkacc[db][4 * r4], dkacc[db][4 * r4 + 1], dkacc[db][4 * r4 + 2], dkacc[db][4 * r4 + 3]};
-        red[((2 * db + 1) * 4 + r4) * 64 + lane] = f32x4{dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]};
+        red_k[r4 * 64 + lane] = f32x4{dkacc[db][4 * r4], dkacc[db][4 * r4 + 1], dkacc[db][4 * r4 + 2], dkacc[db][4 * r4 + 3]};
+        red_v[r4 * 64 + lane] = f32x4{dvacc[db][4 * r4], dvacc[db][4 * r4 + 1], dvacc[db][4 * r4 + 2], dvacc[db][4 * r4 + 3]};
       }
-  }
-  __syncthreads();
-  if (qh == 0) {
-    const int gb = p.grad_bf16 ? 2 : 4;
-    const rsrc_t rdk = make_rsrc((char*)p.dk + sq.dkoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dk_ss * gb) + D * gb : 0u);
-    const rsrc_t rdv = make_rsrc((char*)p.dv + sq.dvoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dv_ss * gb) + D * gb : 0u);
-    const uint32_t dk_row = (uint32_t)my_key * (uint32_t)(p.dk_ss * gb);
-    const uint32_t dv_row = (uint32_t)my_key * (uint32_t)(p.dv_ss * gb);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    }
+    __syncthreads();
+    if (qh == 0) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * db + 8 * r4 + 4 * hl;
-        const f32x4 ok = red[((2 * db) * 4 + r4) * 64 + lane];
-        const f32x4 ov = red[((2 * db + 1) * 4 + r4) * 64 + lane];
+        const f32x4 ok = red_k[r4 * 64 + lane];
+        const f32x4 ov = red_v[r4 * 64 + lane];
         store_grad4(rdk, dk_row + d * 4, dk_row + d * 2, p.grad_bf16, dkacc[db][4 * r4] + ok[0],
                     dkacc[db][4 * r4 + 1] + ok[1], dkacc[db][4 * r4 + 2] + ok[2], dkacc[db][4 * r4 + 3] + ok[3]);
         store_grad4(rdv, dv_row + d * 4, dv_row + d * 2, p.grad_bf16, dvacc[db][4 * r4] + ov[0],
                     dvacc[db][4 * r4 + 1] + ov[1], dvacc[db][4 * r4 + 2] + ov[2], dvacc[db][4 * r4 + 3] + ov[3]);
       }
+    }
   }
 }
 
