@@ -100,6 +100,12 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// max(a, b, c) as one v_maximum3_f32.  NaN-propagating (IEEE maximum), so unlike
+// fmaxf it needs no canonicalising copies of operands that come out of an MFMA.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // Combine a value with the same lane's value in the other half of the wave
 // (lane l and lane l ^ 32) using v_permlane32_swap.
 __device__ __forceinline__ float half_swap_max(float x) {

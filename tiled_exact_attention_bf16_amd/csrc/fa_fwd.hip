@@ -227,18 +227,25 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
           }
         }
       }
-      if constexpr (NEXT && PREV) {
-        // keep the interleave: K reads run three MFMAs ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    if constexpr (PREV) {
+      // the empty asm makes the sum exist here, so its adds are scheduled among
+      // this phase's MFMAs instead of being sunk past the rescale branch
+      lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      asm volatile("" : "+v"(lsum));
+    }
+    if constexpr (NEXT && PREV) {
+      // interleave: K reads run three MFMAs ahead across both key blocks, seven
+      // vector instructions (fma, exp, add for two scores, one cvt) per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7 * UPD, 0);
-          if (ds < NDS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+      for (int i = 0; i < NKB * NDS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7 * UPD, 0);
+        if (i < NKB * NDS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    if constexpr (PREV) lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // mask S(j) (the diagonal tiles under the causal mask and the ragged last tile)
     if constexpr (NEXT && MASK) {
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
             const int i = g * NDB + db;
 #pragma unroll
             for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
-              mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_next[q >> 4][q & 15], s_next[q >> 4][(q & 15) + 1]));
+              mx = max3(mx, s_next[q >> 4][q & 15], s_next[q >> 4][(q & 15) + 1]);
           }
         }
       }
@@ -289,11 +296,13 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
         if (i < BN / 16 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       lsum_r += rsr[0] + rsr[1];
+      asm volatile("" : "+v"(lsum_r));  // as for lsum: keep the dot2 sums in this phase
+      __builtin_amdgcn_sched_barrier(0);
     } else if constexpr (NEXT) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s_next[kb][r]);
+        for (int r = 0; r < 16; r += 2) mx = max3(mx, s_next[kb][r], s_next[kb][r + 1]);
     }
 
     if constexpr (NEXT) {
@@ -660,7 +669,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
             const int i = g * NDB + db;
 #pragma unroll
             for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
-              mxa = __builtin_fmaxf(mxa, __builtin_fmaxf(sa_next[q >> 4][q & 15], sa_next[q >> 4][(q & 15) + 1]));
+              mxa = max3(mxa, sa_next[q >> 4][q & 15], sa_next[q >> 4][(q & 15) + 1]);
           }
           B.o[db] = mfma_bf16(va, pbb[g], B.o[db]);
 #pragma unroll
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
             const int i = g * NDB + db;
 #pragma unroll
             for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
-              mxb = __builtin_fmaxf(mxb, __builtin_fmaxf(sb_next[q >> 4][q & 15], sb_next[q >> 4][(q & 15) + 1]));
+              mxb = max3(mxb, sb_next[q >> 4][q & 15], sb_next[q >> 4][(q & 15) + 1]);
           }
         }
       }
