@@ -356,6 +356,18 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
         s = mfma_bf16(lds_read16(qt + arow + co), lds_read16(k_lds + brow + co), s);
         dp = mfma_bf16(lds_read16(dot + arow + co), lds_read16(v_lds + brow + co), dp);
       }
+      // hidden keys (the causal diagonal, the ragged last block): their scores become
+      // -inf, so P and dS' are exactly 0.  A wave-uniform branch, so that the other
+      // steps carry no mask arithmetic.
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int query = row0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          bool hide = my_key >= Lk;
+          if constexpr (CAUSAL) hide = hide || my_key > query + coff;
+          s[r] = hide ? -INFINITY : s[r];
+        }
+      }
       u32x4 pb[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -368,13 +380,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
           float pv[4], dsv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float pe = exp2_hw(__builtin_fmaf(s[4 * r4 + j], c, -l2[j]));
-            if (need_mask) {
-              const int query = row0 + 8 * r4 + 4 * hl + j;
-              bool hide = my_key >= Lk;
-              if constexpr (CAUSAL) hide = hide || my_key > query + coff;
-              pe = hide ? 0.0f : pe;
-            }
+            const float pe = exp2_hw(__builtin_fmaf(s[4 * r4 + j], c, -l2[j]));
             pv[j] = pe;
             dsv[j] = pe * __builtin_fmaf(dp[4 * r4 + j], p.scale, -dd[j]);  // scale * P (dP - D)
           }
