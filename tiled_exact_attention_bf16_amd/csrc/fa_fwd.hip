@@ -196,53 +196,52 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const FA_LDS char* vt = vbuf(PAR ^ 1);
     const int k0 = j * BN;
 
-    // -- phase 1, one 32-key block at a time: the NDS MFMAs of S(j)'s block kb, each
-    // followed by 16/NDS exponentials of tile j-1's block kb (with their sums and
-    // bf16 packing), so the previous scores die as the new ones appear --
-    constexpr int UPD = 8 / NDS;  // pairs of scores per MFMA
+    // -- phase 1: S(j)'s MFMAs, with the exponentials of tile j-1's first 32-key
+    // block (with their sums and bf16 packing) between them.  The second block's
+    // exponentials run beside the first half of phase 2, whose PV products only need
+    // the first block's weights: the vector work (an exponential costs four FMA
+    // issue slots) is then spread over 24 of the step's 32 MFMAs instead of 16 --
     u32x4 pb[2 * NKB];
     float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four partial sums: short dependency chains
+    auto exp_pair = [&](const int q) {  // scores 2u, 2u+1 of block kb = q / 8 of tile j-1
+      const int kb = q >> 3, u = q & 7, e = 2 * u;
+      // P = 2^(s*c - m*c) -> bf16 operands; the fp32 weights feed the LSE sum
+      const float x0 = __builtin_fmaf(s_prev[kb][e], c, -mref);
+      const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref);
+      const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
+      const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
+      rs[u & 3] += p0;
+      rs[u & 3] += p1;
+      pb[2 * kb + (u >> 2)][u & 3] = pack_bf16(p0, p1);
+    };
+    constexpr int NPAIR = 8 * NKB;   // pairs of scores per lane and tile
+    constexpr int P1 = 8;            // pairs of phase 1: the first block
+    constexpr int NM1 = NKB * NDS;   // MFMAs of phase 1
+    static_assert(NKB == 2, "two 32-key blocks per tile");
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if constexpr (NEXT) s_next[kb] = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
+        const int i = kb * NDS + ds;
         if constexpr (NEXT) {
           const u32x4 a = lds_read16(kt + 32 * kb * ROWB + off_k[ds]);
           s_next[kb] = mfma_bf16(a, qreg[ds], s_next[kb]);
         }
         if constexpr (PREV) {
 #pragma unroll
-          for (int uu = 0; uu < UPD; ++uu) {
-            // P = 2^(s*c - m*c) -> bf16 operands; the fp32 weights feed the LSE sum
-            const int u = ds * UPD + uu;
-            const int e = 2 * u;
-            const float x0 = __builtin_fmaf(s_prev[kb][e], c, -mref);
-            const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref);
-            const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
-            const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
-            rs[u & 3] += p0;
-            rs[u & 3] += p1;
-            pb[2 * kb + (u >> 2)][u & 3] = pack_bf16(p0, p1);
-          }
+          for (int q = i * P1 / NM1; q < (i + 1) * P1 / NM1; ++q) exp_pair(q);
         }
       }
     }
-    if constexpr (PREV) {
-      // the empty asm makes the sum exist here, so its adds are scheduled among
-      // this phase's MFMAs instead of being sunk past the rescale branch
-      lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-      asm volatile("" : "+v"(lsum));
-    }
     if constexpr (NEXT && PREV) {
-      // interleave: K reads run three MFMAs ahead across both key blocks, seven
-      // vector instructions (fma, exp, add for two scores, one cvt) per MFMA
+      // K reads run three MFMAs ahead
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int i = 0; i < NKB * NDS; ++i) {
+      for (int i = 0; i < NM1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7 * UPD, 0);
-        if (i < NKB * NDS - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (i < NM1 - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -262,41 +261,57 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
         }
     }
 
-    // -- phase 2: O^T += V^T P^T, each MFMA followed by a step of the row-sum of the
-    // rounded weights or of the row maximum of S(j) --
+    // -- phase 2: O^T += V^T P^T; the first half's MFMAs (keys of the first block)
+    // carry the second block's exponentials, every MFMA a step of the row maximum of
+    // S(j), and the second half the row sum of the rounded weights --
     float mx = -INFINITY;
     if constexpr (PREV) {
       float rsr[2] = {0.0f, 0.0f};
+      constexpr int NM2 = BN / 16 * NDB;  // MFMAs of phase 2
 #pragma unroll
       for (int g = 0; g < BN / 16; ++g) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
+          const int i = g * NDB + db;
+#pragma unroll
+          for (int q = P1 + i * (NPAIR - P1) / (NM2 / 2); q < P1 + (i + 1) * (NPAIR - P1) / (NM2 / 2) && q < NPAIR; ++q)
+            exp_pair(q);
           const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
           const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
           oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
-          // sum of the bf16-rounded weights the product used: O is normalised by
-          // it, so a dominant weight's rounding cancels between numerator and
-          // denominator (with a stale reference that weight is up to 2^8, not 1)
-#pragma unroll
-          for (int e = db * 4 / NDB; e < (db + 1) * 4 / NDB; ++e) rsr[e & 1] = add_bf16_pair(pb[g][e], rsr[e & 1]);
           if constexpr (NEXT) {
             // two scores of S(j) per MFMA, 32 in all
-            const int i = g * NDB + db;
 #pragma unroll
-            for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
+            for (int q = i * 32 / NM2; q < (i + 1) * 32 / NM2; q += 2)
               mx = max3(mx, s_next[q >> 4][q & 15], s_next[q >> 4][(q & 15) + 1]);
           }
         }
       }
+      // sum of the bf16-rounded weights the products used: O is normalised by it, so
+      // a dominant weight's rounding cancels between numerator and denominator (with a
+      // stale reference that weight is up to 2^8, not 1)
+#pragma unroll
+      for (int g = 0; g < BN / 16; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rsr[e & 1] = add_bf16_pair(pb[g][e], rsr[e & 1]);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-      for (int i = 0; i < BN / 16 * NDB; ++i) {
+      for (int i = 0; i < NM2 / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = NM2 / 2; i < NM2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        if (i < BN / 16 * NDB - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i < NM2 - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      // the empty asm makes the sums exist here, so their adds are scheduled among
+      // this phase's MFMAs instead of being sunk past the rescale branch
+      lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
       lsum_r += rsr[0] + rsr[1];
-      asm volatile("" : "+v"(lsum_r));  // as for lsum: keep the dot2 sums in this phase
+      asm volatile("" : "+v"(lsum), "+v"(lsum_r));
       __builtin_amdgcn_sched_barrier(0);
     } else if constexpr (NEXT) {
 #pragma unroll
