@@ -140,6 +140,18 @@ fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tunin
 /* Query rows per forward work item for the given tuning (NULL = defaults). */
 int32_t fa_fwd_tile_rows(const fa_fwd_tuning* tuning);
 
+/* Diagnostic: evaluates, for n fp32 values x (device), the two ways the forward
+ * forms the softmax weights 2^x -- the software exponential that splits x into an
+ * integer and a fraction, evaluates a cubic on the fraction with multiply-adds and
+ * adds the integer to the exponent bits (FA4 summary page, "Software exponentials"
+ * bullet; lecompute.fr article, section "Move some exponential work to different
+ * units"), into y_poly, and the hardware v_exp_f32 into y_hw -- exactly as the
+ * forward kernel evaluates them.  The software path is valid for x <= 8 (the lazy
+ * rescale bound) and returns 0 for x < -126.  All three arrays are caller-owned
+ * device memory of n floats; n = 0 does nothing; n < 0 or a NULL array with n > 0
+ * is FA_ERR_INVALID_ARGUMENT.  Enqueued on `stream`. */
+fa_status fa_exp2_probe(const float* x, float* y_poly, float* y_hw, int64_t n, void* stream);
+
 /* Arguments of the backward pass. */
 typedef struct fa_bwd_args {
   const void* q;         /* bf16, as in the forward                                */

@@ -231,3 +231,10 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(L.FaLibraryMissing):
         L.lib()
+
+
+def test_exp2_probe_validation():
+    lib = L.lib()
+    assert lib.fa_exp2_probe(None, None, None, -1, None) == L.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_exp2_probe(None, None, None, 5, None) == L.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_exp2_probe(None, None, None, 0, None) == L.FA_OK  # nothing to do, no device call

@@ -76,6 +76,7 @@ SIGNATURES = {
     "fa_fwd": (c_int32, [POINTER(FwdArgs), POINTER(FwdTuning), c_void_p, c_size_t, c_void_p]),
     "fa_fwd_build_schedule": (c_int32, [POINTER(FwdArgs), POINTER(FwdTuning), c_void_p, c_size_t, c_void_p]),
     "fa_fwd_tile_rows": (c_int32, [POINTER(FwdTuning)]),
+    "fa_exp2_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
     "fa_bwd_workspace_size": (c_int32, [POINTER(BwdArgs), POINTER(c_size_t)]),
     "fa_bwd": (c_int32, [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
     "fa_bwd_phases": (c_int32, [POINTER(BwdArgs), c_int32, c_void_p, c_size_t, c_void_p]),

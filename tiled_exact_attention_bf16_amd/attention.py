@@ -127,6 +127,16 @@ def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[T
     return int(lib.fa_fwd_tile_rows(ctypes.byref(t))), items
 
 
+def exp2_probe(x: torch.Tensor, stream=None):
+    """(software 2^x, hardware v_exp_f32) of a contiguous fp32 device tensor, as the
+    forward kernel evaluates them (fa_exp2_probe)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 device tensor")
+    y_poly, y_hw = torch.empty_like(x), torch.empty_like(x)
+    L.check(L.lib().fa_exp2_probe(_ptr(x), _ptr(y_poly), _ptr(y_hw), x.numel(), _stream(stream)), "fa_exp2_probe")
+    return y_poly, y_hw
+
+
 def bwd_args(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale, causal, deterministic, grad_dtype,
              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None) -> L.BwdArgs:
     varlen = cu_seqlens_q is not None

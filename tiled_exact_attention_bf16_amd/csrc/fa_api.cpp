@@ -240,6 +240,12 @@ fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tunin
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_exp2_probe(const float* x, float* y_poly, float* y_hw, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (x == nullptr || y_poly == nullptr || y_hw == nullptr))) return FA_ERR_INVALID_ARGUMENT;
+  hipError_t e = fa::launch_exp2_probe(x, y_poly, y_hw, n, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* workspace, size_t workspace_bytes,
                  void* stream) {
   Shape s;

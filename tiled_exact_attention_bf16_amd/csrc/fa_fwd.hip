@@ -874,6 +874,26 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const 
   }
 }
 
+// ---- probe of the two exponentials the forward uses ----
+// y_poly[i] = the software 2^x (integer/fraction split and cubic on the multiply-add
+// units) and y_hw[i] = v_exp_f32, both exactly as the forward evaluates them.
+__global__ __launch_bounds__(256) void exp2_probe_kernel(const float* x, float* y_poly, float* y_hw, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = x[i];
+    y_poly[i] = exp2_poly(v);
+    y_hw[i] = exp2_hw(v);
+  }
+}
+
+hipError_t launch_exp2_probe(const float* x, float* y_poly, float* y_hw, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(exp2_probe_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, x,
+                     y_poly, y_hw, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int tile_rows,
                                int block_n, bool causal, int32_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, batch, tile_rows, block_n,

@@ -59,6 +59,9 @@ hipError_t launch_fwd(const FwdParams& p, const FwdConfig& cfg, hipStream_t stre
 hipError_t launch_fwd_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int tile_rows,
                                int block_n, bool causal, int32_t* out, hipStream_t stream);
 
+// Evaluates the forward's software and hardware 2^x on n device values.
+hipError_t launch_exp2_probe(const float* x, float* y_poly, float* y_hw, int64_t n, hipStream_t stream);
+
 struct BwdParams {
   const void* q;
   const void* k;
