@@ -57,7 +57,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride, ... */
-  FA_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  FA_ERR_UNSUPPORTED = 2,        /* valid request the library does not implement  */
   FA_ERR_WORKSPACE_TOO_SMALL = 3,
   FA_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
 } fa_status;
