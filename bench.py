@@ -199,7 +199,6 @@ def main():
     ap.add_argument("--q-tiles", type=int, default=-1)
     ap.add_argument("--poly", type=int, default=-1)
     ap.add_argument("--tau", type=int, default=-1)
-    ap.add_argument("--rows-per-wave", type=int, default=-1)
     ap.add_argument("--all-configs", action="store_true",
                     help="also time forward and backward of every named workload (median/min of 50)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -232,7 +231,7 @@ def main():
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
     ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")   # >= either mode's workspace (fp32 dQ accumulator)
-    tuning = FA.Tuning(args.poly, args.tau, args.q_tiles, args.rows_per_wave)
+    tuning = FA.Tuning(args.poly, args.tau, args.q_tiles)
     det = not args.atomic
 
     def fwd():

@@ -86,58 +86,85 @@ typedef struct fa_fwd_args {
   int32_t max_seqlen_k;
   int32_t total_q;       /* variable length: T_q = cu_seqlens_q[batch]             */
   int32_t total_k;
-  float softmax_scale;   /* finite and >= 0, e.g. 1/sqrt(D)                       */
+  float softmax_scale;   /* finite and > 0, e.g. 1/sqrt(D); else see fa_fwd       */
   int32_t causal;        /* 0 or 1                                                 */
 } fa_fwd_args;
 
-/* Optional forward variant selection (NULL = defaults).  Both knobs select among
- * compiled kernel instances; values without an instance give FA_ERR_UNSUPPORTED. */
+/* Optional forward variant selection (NULL = defaults).  The knobs select among
+ * compiled kernel instances; values without an instance give FA_ERR_UNSUPPORTED.
+ * The defaults (hardware exponential only, threshold 8, two query tiles, key split
+ * chosen from the shape) are the fast path; the other values exist so that each
+ * of the method's choices can be measured against its alternative, and the
+ * exp2-share and threshold alternatives are compiled for head_dim 128 with fixed
+ * length only. */
 typedef struct fa_fwd_tuning {
   /* Of every 16 score registers of a lane, how many take the FMA-only exp2
    * (integer/fraction split, cubic on the fraction, integer added to the exponent
    * field; fdeinterviews.com FA4 summary, "Software exponentials" bullet) instead of
-   * the hardware v_exp_f32.  Compiled: 0, 2, 4.  -1 = default. */
+   * the hardware v_exp_f32.  Compiled: 0, 2, 4.  -1 = default (0, the measured
+   * fastest). */
   int32_t exp2_poly_per16;
   /* Lazy rescale threshold in log2 units (fdeinterviews.com FA4 summary, "Lazy
    * rescaling" bullet): the output is rescaled only when a row's maximum grows by
    * more than this.  Compiled: 8 (the method) and 0 (eager).  -1 = default (8). */
   int32_t rescale_threshold_log2;
   /* Query tiles of 128 rows interleaved per workgroup (two wave sets sharing each
-   * K/V stage).  Compiled: 1, 2.  -1 = default.  Must be 2 or -1 with 64-row waves. */
+   * K/V stage; fdeinterviews.com FA4 summary, "Pipeline for asynchronous tensor
+   * cores" bullet).  Compiled: 1, 2.  -1 = default (2). */
   int32_t q_tiles_per_workgroup;
-  /* Query rows per wave: 32 (two waves per SIMD, 32x32 tiles) or 64 (one wave per
-   * SIMD owning two 32-row blocks, each K/V fragment read once for both; 256-row
-   * workgroups).  0 or negative = default. */
-  int32_t rows_per_wave;
   /* Split of each sequence's keys into this many contiguous chunks, each handled
    * by its own workgroups (128-row query tiles); every chunk writes a partial O
    * (fp32) and LSE to the workspace and a merge pass combines them:
    * LSE = ln sum_c e^LSE_c, O = sum_c e^(LSE_c - LSE) O_c.  For short query
-   * sequences against long key sequences (generation with a cache), where the
-   * query tiles alone cannot fill the GPU.  1 = no split; 2..64 = that many;
-   * 0 or negative = chosen from the shape. */
+   * sequences against long key sequences (generation with a cache; fdeinterviews.com
+   * FA4 summary, paragraph on long-context inference and training), where the query
+   * tiles alone cannot fill the GPU.  1 = no split; 2..64 = that many; 0 or negative =
+   * chosen from the shape. */
   int32_t key_splits;
 } fa_fwd_tuning;
 
 /* Bytes of device workspace fa_fwd needs for `a` and `tuning` (NULL = defaults):
- * room for the longest-first work list of variable-length batches and for the
- * partial results of a key split; 0 when neither is used. */
+ * room for the longest-first work list of variable-length batches (fdeinterviews.com
+ * FA4 summary, features paragraph) and for the partial results of a key split; 0
+ * when neither is used.  Validates `a` and `tuning` exactly as fa_fwd does and
+ * returns the same status; `bytes` must not be NULL (FA_ERR_INVALID_ARGUMENT).  No
+ * HIP call is made. */
 fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tuning, size_t* bytes);
 
-/* Forward pass: writes O and LSE.  `workspace` (device, 256-byte aligned, at least
- * fa_fwd_workspace_size bytes, contents ignored on entry) may be NULL when that
- * size is 0. */
+/* Forward pass (lecompute.fr FA4 article, section "Between the matrix products the
+ * kernel must produce weights"; fdeinterviews.com FA4 summary, opening paragraph,
+ * "Lazy rescaling" and "Software exponentials" bullets): writes O (bf16, layout of
+ * q) and LSE (fp32, natural log, scale included) for every query row, tiling Q
+ * against K/V with an online softmax so that no score reaches device memory.
+ * `workspace` (device, 256-byte aligned, at least fa_fwd_workspace_size bytes,
+ * contents ignored on entry and clobbered) may be NULL when that size is 0.
+ * Errors, all reported before any device work is enqueued:
+ *   FA_ERR_INVALID_ARGUMENT  NULL or misaligned pointer, negative size, stride
+ *                            smaller than head_dim or not a multiple of 8
+ *                            elements, causal not 0/1, non-finite scale;
+ *   FA_ERR_UNSUPPORTED       head_dim not 64/128, scale <= 0 (the kernels fold
+ *                            the scale into the exponent after taking row maxima
+ *                            of the raw scores, which needs a positive scale),
+ *                            offsets beyond 2^31 bytes per sequence, sequences
+ *                            longer than 524,288, a tuning without an instance;
+ *   FA_ERR_WORKSPACE_TOO_SMALL  workspace NULL or smaller than required;
+ *   FA_ERR_HIP               a kernel launch failed.
+ * An empty batch (batch = 0 or no query rows) returns FA_OK with no work. */
 fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* workspace,
                  size_t workspace_bytes, void* stream);
 
 /* Builds only the longest-first work list of a variable-length forward into
- * `workspace` (the first step of fa_fwd for variable length), so that it can be
- * inspected.  Layout: int32 count n, then n pairs {sequence, query tile}, tiles of
- * `fa_fwd_tile_rows` rows, in dispatch order (each item is run for every head). */
+ * `workspace` (the first step of fa_fwd for variable length; fdeinterviews.com FA4
+ * summary, features paragraph: tiles are dispatched most expensive first), so that
+ * it can be inspected.  Layout: int32 count n, then n pairs {sequence, query tile},
+ * tiles of `fa_fwd_tile_rows` rows, in dispatch order, cost (key tiles visited)
+ * non-increasing; items of equal cost may come in any order.  Errors as fa_fwd,
+ * plus FA_ERR_INVALID_ARGUMENT for a fixed-length `a`. */
 fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tuning,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Query rows per forward work item for the given tuning (NULL = defaults). */
+/* Query rows per forward work item for the given tuning (NULL = defaults): the
+ * tile size of the work list above.  0 for a tuning without an instance. */
 int32_t fa_fwd_tile_rows(const fa_fwd_tuning* tuning);
 
 /* Diagnostic: evaluates, for n fp32 values x (device), the two ways the forward
@@ -188,14 +215,26 @@ typedef struct fa_bwd_args {
   int32_t grad_dtype;    /* FA_DTYPE_F32 (default) or FA_DTYPE_BF16                */
 } fa_bwd_args;
 
-/* Bytes of device workspace fa_bwd needs (fp32 dQ accumulator, row terms
- * D_i = sum_d dO_id O_id, work lists). */
+/* Bytes of device workspace fa_bwd needs for `a`: the fp32 dQ accumulator (atomic
+ * mode only), the row terms D_i = sum_d dO_id O_id and the work lists of
+ * variable-length batches.  Validates `a` exactly as fa_bwd does and returns the
+ * same status; `bytes` must not be NULL.  No HIP call is made. */
 fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes);
 
-/* Backward pass: writes dQ, dK, dV.  `workspace` as for fa_fwd (required). */
+/* Backward pass (fdeinterviews.com FA4 summary, "Paired-CTA backward pass" bullet
+ * and features paragraph: a backward from the saved log-sum-exp whose dQ is added
+ * with atomics, with a deterministic mode): writes dQ, dK, dV (grad_dtype, layouts
+ * of q, k, v) of the loss whose gradient with respect to O is dout, recomputing the
+ * softmax weights from q, k and lse; the equations are the textbook gradient of
+ * softmax attention (dV = P^T dO, dS = P o (dO V^T - D), dQ = scale dS K,
+ * dK = scale dS^T Q).  deterministic = 1 reduces dQ in a fixed order (bit-identical
+ * results from run to run on one GPU); 0 adds it with fp32 atomics.  `workspace` as
+ * for fa_fwd (required: the row terms always live there).  Errors as for fa_fwd,
+ * plus FA_ERR_INVALID_ARGUMENT for deterministic or grad_dtype out of range. */
 fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The backward's three phases, enqueued in this order by fa_bwd:
+/* The backward of fa_bwd (same passages, arguments and errors) split into its three
+ * phases, enqueued in this order by fa_bwd:
  *   FA_BWD_PHASE_PRE:  row terms D_i = sum_d dO_id O_id into the workspace (and, in
  *                      atomic mode, zeroing of the fp32 dQ accumulator);
  *   FA_BWD_PHASE_MAIN: the key-block kernel: dK and dV (and, in atomic mode, dQ
@@ -206,15 +245,19 @@ fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, 
  * fa_bwd_phases runs the selected subset (a bitwise OR) on the same arguments and
  * workspace, so callers can time or interleave them; a phase reads what the earlier
  * phases left in the workspace, so running MAIN without a preceding PRE on that
- * workspace gives undefined gradients. */
+ * workspace gives undefined gradients.  `phases` outside 1..7 is
+ * FA_ERR_INVALID_ARGUMENT. */
 enum { FA_BWD_PHASE_PRE = 1, FA_BWD_PHASE_MAIN = 2, FA_BWD_PHASE_POST = 4, FA_BWD_PHASE_ALL = 7 };
 fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, size_t workspace_bytes,
                         void* stream);
 
-/* Static description of a status code (never NULL). */
+/* Static name of a status code, e.g. "FA_ERR_UNSUPPORTED" ("FA_ERR_UNKNOWN" for a
+ * value outside the enum; never NULL).  The codes are this library's own; the
+ * pages define no interface (the argument set follows the operation: Q, K, V, the
+ * softmax scale, the causal flag and packed lengths). */
 const char* fa_status_str(fa_status s);
 
-/* Library version string. */
+/* Library version string (static, never NULL). */
 const char* fa_version(void);
 
 #ifdef __cplusplus

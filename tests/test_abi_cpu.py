@@ -50,7 +50,7 @@ def fwd_args(b=2, s=256, h=4, d=128, causal=0, scale=0.088):
 
 def ws_size(a, tuning=None):
     n = ctypes.c_size_t(123)
-    t = tuning if tuning is not None else L.FwdTuning(-1, -1, -1, -1, -1)
+    t = tuning if tuning is not None else L.FwdTuning(-1, -1, -1, -1)
     st = L.lib().fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(t), ctypes.byref(n))
     return st, n.value
 
@@ -76,6 +76,8 @@ def test_fixed_length_forward_needs_no_workspace():
     (lambda a: setattr(a, "softmax_scale", float("nan")), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "softmax_scale", float("inf")), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "softmax_scale", -1.0), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "softmax_scale", 0.0), L.FA_ERR_UNSUPPORTED),    # scale must be > 0
+    (lambda a: setattr(a, "softmax_scale", -0.0), L.FA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "causal", 2), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "q_stride", L.Strides(256 * 512, 500, 128)), L.FA_ERR_INVALID_ARGUMENT),  # stride % 8
     (lambda a: setattr(a, "o_stride", L.Strides(256 * 512, 64, 128)), L.FA_ERR_INVALID_ARGUMENT),   # rows overlap D
@@ -94,11 +96,21 @@ def test_forward_validation(mutate, expect):
     ((2, 0, -1), L.FA_ERR_UNSUPPORTED),
     ((-1, 5, -1), L.FA_ERR_UNSUPPORTED),
     ((-1, -1, 3), L.FA_ERR_UNSUPPORTED),
-    ((-1, -1, -1, 48), L.FA_ERR_UNSUPPORTED),
-    ((-1, -1, 1, 64), L.FA_ERR_UNSUPPORTED),   # 64-row waves come in 256-row workgroups only
+    ((-1, -1, -1, 65), L.FA_ERR_UNSUPPORTED),
 ])
 def test_forward_tuning_validation(tuning, expect):
     assert fwd_status(fwd_args(), L.FwdTuning(*tuning)) == expect
+
+
+@pytest.mark.parametrize("tuning", [(2, 8, -1), (4, -1, 1), (0, 0, 2)])
+def test_measurement_variants_need_d128_fixed_length(tuning):
+    # the exp2-share and eager-threshold instances exist for head_dim 128, fixed length
+    t = L.FwdTuning(*tuning)
+    assert ws_size(fwd_args(d=128), t)[0] == L.FA_OK
+    assert ws_size(fwd_args(d=64), t)[0] == L.FA_ERR_UNSUPPORTED
+    assert fwd_status(fwd_args(d=64), t) == L.FA_ERR_UNSUPPORTED
+    assert ws_size(varlen_args(), t)[0] == L.FA_ERR_UNSUPPORTED
+    assert ws_size(varlen_args(), L.FwdTuning(0, 8, -1))[0] == L.FA_OK
 
 
 def test_tile_rows():
@@ -106,8 +118,7 @@ def test_tile_rows():
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 1))) == 128
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 2))) == 256
     assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 7))) == 0
-    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, -1, 64))) == 256
-    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, 1, 64))) == 0
+    assert lib.fa_fwd_tile_rows(ctypes.byref(L.FwdTuning(-1, -1, -1, 4))) == 128   # key split: 128-row tiles
 
 
 def varlen_args(n_seq=32, total=131072, max_len=16384, causal=1, h=16, d=128):
@@ -181,15 +192,14 @@ def test_backward_workspace_sizes():
 def test_key_split_workspace_and_validation():
     a = fwd_args(b=2, s=256, h=4, d=128)
     a.seqlen_q, a.seqlen_k = 8, 16384
-    assert ws_size(a, L.FwdTuning(-1, -1, -1, -1, 1)) == (L.FA_OK, 0)          # split off: no workspace
-    st, n = ws_size(a, L.FwdTuning(-1, -1, -1, -1, 4))
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, 1)) == (L.FA_OK, 0)              # split off: no workspace
+    st, n = ws_size(a, L.FwdTuning(-1, -1, -1, 4))
     rows = 4 * 4 * 2 * 8                                                   # splits * heads * total_q
     assert st == L.FA_OK and n >= rows * 4 + rows * 128 * 4 and n % 256 == 0
     st, n_auto = ws_size(a)                                                # 8 work items: split chosen
     assert st == L.FA_OK and n_auto > 0
-    assert ws_size(a, L.FwdTuning(-1, -1, -1, -1, 65))[0] == L.FA_ERR_UNSUPPORTED
-    assert ws_size(a, L.FwdTuning(-1, -1, -1, 64, 2))[0] == L.FA_ERR_UNSUPPORTED
-    assert fwd_status(a, L.FwdTuning(-1, -1, -1, -1, 4), ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, 65))[0] == L.FA_ERR_UNSUPPORTED
+    assert fwd_status(a, L.FwdTuning(-1, -1, -1, 4), ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
     big = fwd_args()                                                       # many work items: no split
     assert ws_size(big) == (L.FA_OK, 0)
 
@@ -210,6 +220,7 @@ def test_causal_with_unequal_lengths_is_accepted():
     (lambda a: setattr(a, "deterministic", 3), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "grad_dtype", 7), L.FA_ERR_INVALID_ARGUMENT),
     (lambda a: setattr(a, "head_dim", 256), L.FA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "softmax_scale", 0.0), L.FA_ERR_UNSUPPORTED),
     (lambda a: setattr(a, "dk_stride", L.Strides(256 * 512, 130, 128)), L.FA_ERR_INVALID_ARGUMENT),
 ])
 def test_backward_validation(mutate, expect):

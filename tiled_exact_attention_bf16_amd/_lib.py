@@ -51,7 +51,7 @@ class FwdArgs(ctypes.Structure):
 
 class FwdTuning(ctypes.Structure):
     _fields_ = [("exp2_poly_per16", c_int32), ("rescale_threshold_log2", c_int32),
-                ("q_tiles_per_workgroup", c_int32), ("rows_per_wave", c_int32), ("key_splits", c_int32)]
+                ("q_tiles_per_workgroup", c_int32), ("key_splits", c_int32)]
 
 
 class BwdArgs(ctypes.Structure):

@@ -18,17 +18,84 @@ from . import _lib as L
 @dataclass
 class Tuning:
     """Forward variant: FMA-exp2 share (of 16), lazy threshold (log2 units), query tiles per
-    workgroup, query rows per wave (32 or 64), key splits (1 = none).  -1 keeps the
-    library default."""
+    workgroup, key splits (1 = none).  -1 keeps the library default."""
     exp2_poly_per16: int = -1
     rescale_threshold_log2: int = -1
     q_tiles_per_workgroup: int = -1
-    rows_per_wave: int = -1
     key_splits: int = -1
 
     def c(self):
         return L.FwdTuning(self.exp2_poly_per16, self.rescale_threshold_log2, self.q_tiles_per_workgroup,
-                           self.rows_per_wave, self.key_splits)
+                           self.key_splits)
+
+
+# ---- argument checks: the C library sees only pointers and sizes, so the tensors'
+# dtype, shape and device are checked here before any pointer is handed over (all
+# dtype and shape checks first, then the devices) ----
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(name: str, t, dtype: torch.dtype, shape: tuple) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_devices(**tensors) -> None:
+    """Every tensor on the GPU, and all on the device of the first one."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _need(t.device.type == "cuda", f"{name} must be a GPU tensor, got device {t.device}")
+        dev = t.device if dev is None else dev
+        _need(t.device == dev, f"{name} is on {t.device}, expected {dev} (all tensors on one device)")
+
+
+def _check_lengths(name: str, cu) -> None:
+    _need(isinstance(cu, torch.Tensor) and cu.dtype == torch.int32 and cu.dim() == 1 and cu.numel() >= 1,
+          f"{name} must be a 1-D int32 tensor of batch+1 prefix sums")
+    _need(cu.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k) -> None:
+    """Dtypes and shapes of the inputs: [B, S, H, D] (fixed length) or [T, H, D] (packed)."""
+    varlen = cu_seqlens_q is not None
+    rank = 3 if varlen else 4
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+        _need(t.dtype == torch.bfloat16, f"{name} must be torch.bfloat16, got {t.dtype}")
+        _need(t.dim() == rank, f"{name} must be {'[T, H, D]' if varlen else '[B, S, H, D]'}, got {tuple(t.shape)}")
+    _need(tuple(v.shape) == tuple(k.shape), f"v must have the shape of k {tuple(k.shape)}, got {tuple(v.shape)}")
+    _need(q.shape[-1] == k.shape[-1], f"q and k must share the head dimension ({q.shape[-1]} vs {k.shape[-1]})")
+    _need(q.shape[-2] == k.shape[-2], f"q and k must have the same number of heads ({q.shape[-2]} vs {k.shape[-2]})")
+    if varlen:
+        _check_lengths("cu_seqlens_q", cu_seqlens_q)
+        if cu_seqlens_k is not None:
+            _check_lengths("cu_seqlens_k", cu_seqlens_k)
+            _need(cu_seqlens_k.numel() == cu_seqlens_q.numel(), "cu_seqlens_k must have as many entries as cu_seqlens_q")
+    else:
+        _need(q.shape[0] == k.shape[0], f"q and k must have the same batch ({q.shape[0]} vs {k.shape[0]})")
+        _need(cu_seqlens_k is None, "cu_seqlens_k without cu_seqlens_q")
+
+
+def _lse_shape(q, varlen: bool) -> tuple:
+    return (q.shape[1], q.shape[0]) if varlen else (q.shape[0], q.shape[2], q.shape[1])
+
+
+def _check_lse(lse, q, varlen: bool) -> None:
+    _check_tensor("lse", lse, torch.float32, _lse_shape(q, varlen))
+    # the library writes LSE as a dense [B, H, S_q] / [H, T_q] array
+    _need(lse.is_contiguous(), "lse must be contiguous")
+
+
+def _check_workspace(ws) -> None:
+    if ws is not None:
+        _need(isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8 and ws.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -89,14 +156,21 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Option
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention forward.  Returns (O bf16 like q, LSE fp32 [B,H,S] or [H,T])."""
+    _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     varlen = cu_seqlens_q is not None
+    if out is not None:
+        _check_tensor("out", out, torch.bfloat16, q.shape)
+    if lse is not None:
+        _check_lse(lse, q, varlen)
+    _check_workspace(workspace)
+    _check_devices(q=q, k=k, v=v, out=out, lse=lse, workspace=workspace, cu_seqlens_q=cu_seqlens_q,
+                   cu_seqlens_k=cu_seqlens_k)
     if out is None:
-        out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
-        shape = (q.shape[1], q.shape[0]) if varlen else (q.shape[0], q.shape[2], q.shape[1])
-        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+        lse = torch.empty(_lse_shape(q, varlen), dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, v, out, lse, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     lib = L.lib()
     t = (tuning or Tuning()).c()
@@ -111,6 +185,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Option
 
 def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[Tuning] = None, stream=None):
     """Runs only the variable-length longest-first list builder; returns (tile_rows, [(seq, tile), ...])."""
+    _check_qkv(q, k, k, cu_seqlens, None)
+    _check_devices(q=q, k=k, cu_seqlens=cu_seqlens)
     o = torch.empty_like(q)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     a = fwd_args(q, k, k, o, lse, 1.0, causal, cu_seqlens, None, max_seqlen, None)
@@ -130,7 +206,7 @@ def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[T
 def exp2_probe(x: torch.Tensor, stream=None):
     """(software 2^x, hardware v_exp_f32) of a contiguous fp32 device tensor, as the
     forward kernel evaluates them (fa_exp2_probe)."""
-    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous fp32 device tensor")
     y_poly, y_hw = torch.empty_like(x), torch.empty_like(x)
     L.check(L.lib().fa_exp2_probe(_ptr(x), _ptr(y_poly), _ptr(y_hw), x.numel(), _stream(stream)), "fa_exp2_probe")
@@ -177,10 +253,21 @@ def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
 
     ``phases`` selects a subset of the backward's kernels (fa_bwd_phases); the
     default runs all of them."""
-    if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     if grad_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("grad_dtype must be float32 or bfloat16")
+    _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    varlen = cu_seqlens_q is not None
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    _check_tensor("dout", dout, torch.bfloat16, q.shape)
+    _check_lse(lse, q, varlen)
+    for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g is not None:
+            _check_tensor(name, g, grad_dtype, ref.shape)
+    _check_workspace(workspace)
+    _check_devices(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace,
+                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device) if dv is None else dv

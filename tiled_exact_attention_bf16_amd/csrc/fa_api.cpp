@@ -35,7 +35,10 @@ fa_status check_shape(int batch, int seqlen_q, int seqlen_k, int heads, int d, c
   if (batch < 0 || heads <= 0 || d <= 0) return FA_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
-  if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
+  // The kernels take the row maximum over the raw scores and fold the scale into the
+  // exponent, which needs scale > 0 (scale = 0 would also turn a hidden key's -inf
+  // score times 0 into NaN).
+  if (!(scale > 0.0f)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
   Shape s{};
   s.batch = batch;
@@ -89,7 +92,7 @@ fa_status check_tensor(const void* ptr, const int64_t st[3], const Shape& s, int
 int fwd_max_items(const Shape& s, int tile_rows) { return (s.total_q + tile_rows - 1) / tile_rows + s.batch; }
 
 struct FwdChoice {
-  int poly, tau, qt, rpw, splits;  // splits <= 0: chosen from the shape
+  int poly, tau, qt, splits;  // splits <= 0: chosen from the shape
 };
 
 constexpr int kMaxKeySplits = 64;
@@ -98,7 +101,6 @@ fa_status pick_tuning(const fa_fwd_tuning* t, FwdChoice* c) {
   c->poly = 0;
   c->tau = 8;
   c->qt = 2;
-  c->rpw = 32;
   c->splits = 0;
   if (t == nullptr) return FA_OK;
   if (t->key_splits > kMaxKeySplits) return FA_ERR_UNSUPPORTED;
@@ -106,14 +108,17 @@ fa_status pick_tuning(const fa_fwd_tuning* t, FwdChoice* c) {
   if (t->exp2_poly_per16 >= 0) c->poly = t->exp2_poly_per16;
   if (t->rescale_threshold_log2 >= 0) c->tau = t->rescale_threshold_log2;
   if (t->q_tiles_per_workgroup >= 0) c->qt = t->q_tiles_per_workgroup;
-  if (t->rows_per_wave > 0) c->rpw = t->rows_per_wave;
   if (c->qt != 1 && c->qt != 2) return FA_ERR_UNSUPPORTED;
-  if (c->rpw != 32 && c->rpw != 64) return FA_ERR_UNSUPPORTED;
-  if (c->rpw == 64 && c->qt != 2) return FA_ERR_UNSUPPORTED;
-  if (c->splits > 1 && c->rpw == 64) return FA_ERR_UNSUPPORTED;  // the split path runs 128-row tiles
   if (c->tau == 8 && (c->poly == 0 || c->poly == 2 || c->poly == 4)) return FA_OK;
   if (c->tau == 0 && c->poly == 0) return FA_OK;
   return FA_ERR_UNSUPPORTED;
+}
+
+// The exp2 split shares 2 and 4 and the eager threshold are compiled for head_dim 128
+// and fixed-length batches only (they exist to be measured against the default).
+fa_status check_variant(const Shape& s, const FwdChoice& c) {
+  if (c.poly == 0 && c.tau == 8) return FA_OK;
+  return (s.d == 128 && !s.varlen) ? FA_OK : FA_ERR_UNSUPPORTED;
 }
 
 fa_status check_fwd(const fa_fwd_args* a, Shape* s) {
@@ -135,7 +140,6 @@ fa_status check_fwd(const fa_fwd_args* a, Shape* s) {
 // 16 key tiles of 64.
 int fwd_key_splits(const Shape& s, const FwdChoice& c) {
   if (c.splits > 0) return c.splits;
-  if (c.rpw == 64) return 1;
   const int64_t items = (int64_t)(s.varlen ? fwd_max_items(s, fa::kFwdTileRows)
                                            : (s.max_q + fa::kFwdTileRows - 1) / fa::kFwdTileRows * s.batch) *
                         s.heads;
@@ -218,6 +222,7 @@ fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tunin
   if (st != FA_OK) return st;
   FwdChoice c;
   if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
+  if ((st = check_variant(s, c)) != FA_OK) return st;
   const int splits = fwd_key_splits(s, c);
   *bytes = fwd_ws_layout(s, splits > 1 ? fa::kFwdTileRows : fa::kFwdTileRows * c.qt, splits).total;
   return FA_OK;
@@ -230,6 +235,7 @@ fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tunin
   if (st != FA_OK) return st;
   FwdChoice c;
   if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
+  if ((st = check_variant(s, c)) != FA_OK) return st;
   if (!s.varlen) return FA_ERR_INVALID_ARGUMENT;
   const int tile_rows = fwd_key_splits(s, c) > 1 ? fa::kFwdTileRows : fa::kFwdTileRows * c.qt;
   const size_t need = fwd_ws_layout(s, tile_rows, 1).total;
@@ -253,6 +259,7 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
   if (st != FA_OK) return st;
   FwdChoice c;
   if ((st = pick_tuning(tuning, &c)) != FA_OK) return st;
+  if ((st = check_variant(s, c)) != FA_OK) return st;
   const int splits = fwd_key_splits(s, c);
   if (splits > 1) c.qt = 1;  // the split path runs 128-row tiles
   const int tile_rows = fa::kFwdTileRows * c.qt;
@@ -270,7 +277,7 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
     p.part_lse = (float*)((char*)workspace + ws.lse_off);
     p.part_o = (float*)((char*)workspace + ws.o_off);
   }
-  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, c.rpw, splits};
+  fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, splits};
   hipStream_t strm = (hipStream_t)stream;
   if (s.varlen) {
     hipError_t e = fa::launch_fwd_schedule(s.cu_q, s.cu_k, s.batch, tile_rows, fa::kFwdBlockN, cfg.causal,

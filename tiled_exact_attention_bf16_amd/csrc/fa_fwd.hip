@@ -419,372 +419,6 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
-// ---- 64-row waves: one wave per SIMD, two 32-row blocks per wave ----
-//
-// Same method and step structure as fwd_kernel, but each wave owns 64 query rows
-// (blocks A and B) and runs alone on its SIMD with up to 512 registers.  Every K
-// fragment read from LDS feeds the S MFMAs of both blocks and every V^T fragment
-// both PV MFMAs, so a matrix instruction carries half the LDS reads and half the
-// per-step barrier, DMA-issue and bookkeeping instructions of the 32-row layout;
-// the exponentials and sums of one block run in the shadow of the other block's
-// MFMAs.  A workgroup (four waves) covers the same 256 rows as fwd_kernel<.., 2>.
-template <int NDB>
-struct RowBlock {
-  f32x16 o[NDB];     // O^T accumulators (lane = query row)
-  float m_used;      // reference maximum (raw score units)
-  float mref;        // m_used * c, or 0 while no key was seen
-  float lsum;        // sum of fp32 weights
-  float lsum_r;      // sum of bf16-rounded weights
-};
-
-template <int D, bool CAUSAL, bool VARLEN, int POLY, int TAU>
-__global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdParams p) {
-  constexpr int BN = kFwdBlockN;
-  constexpr int NW = 4;
-  constexpr int WG_ROWS = 256;
-  constexpr int ROWB = D * 2;
-  constexpr int TILE_BYTES = BN * ROWB;
-  constexpr int SLOTS = D / 8;
-  constexpr int NKB = BN / 32;
-  constexpr int NDS = D / 16;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
-  auto kbuf = [&](int par) { return (FA_LDS char*)(par ? k_lds1 : k_lds0); };
-  auto vbuf = [&](int par) { return (FA_LDS char*)(par ? v_lds1 : v_lds0); };
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hl = lane >> 5;
-
-  // ---- work item (as fwd_kernel with 256-row workgroups) ----
-  int b, h, qtile;
-  if constexpr (VARLEN) {
-    const int item = blockIdx.x / p.heads;
-    h = blockIdx.x - item * p.heads;
-    if (item >= p.sched[0]) return;
-    b = p.sched[1 + 2 * item];
-    qtile = p.sched[2 + 2 * item];
-  } else {
-    const int bh_count = p.batch * p.heads;
-    const int t = blockIdx.x / bh_count;
-    const int bh = blockIdx.x - t * bh_count;
-    qtile = CAUSAL ? (p.n_qtiles - 1 - t) : t;
-    b = bh / p.heads;
-    h = bh - b * p.heads;
-  }
-  int Lq = p.seqlen_q, Lk = p.seqlen_k;
-  int64_t qoff, koff, voff, ooff, lseoff;
-  if constexpr (VARLEN) {
-    const int sq = p.cu_q[b], sk = p.cu_k[b];
-    Lq = p.cu_q[b + 1] - sq;
-    Lk = p.cu_k[b + 1] - sk;
-    qoff = sq * p.q_ss + h * p.q_sh;
-    koff = sk * p.k_ss + h * p.k_sh;
-    voff = sk * p.v_ss + h * p.v_sh;
-    ooff = sq * p.o_ss + h * p.o_sh;
-    lseoff = (int64_t)h * p.total_q + sq;
-  } else {
-    qoff = b * p.q_sb + h * p.q_sh;
-    koff = b * p.k_sb + h * p.k_sh;
-    voff = b * p.v_sb + h * p.v_sh;
-    ooff = b * p.o_sb + h * p.o_sh;
-    lseoff = ((int64_t)b * p.heads + h) * Lq;
-  }
-  const int wg_q0 = qtile * WG_ROWS;
-  if (wg_q0 >= Lq) return;
-
-  const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), k_ss2 = (uint32_t)(p.k_ss * 2);
-  const uint32_t v_ss2 = (uint32_t)(p.v_ss * 2), o_ss2 = (uint32_t)(p.o_ss * 2);
-  const rsrc_t rq = make_rsrc((const char*)p.q + qoff * 2, (uint32_t)(Lq - 1) * q_ss2 + ROWB);
-  const rsrc_t rk = make_rsrc((const char*)p.k + koff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * k_ss2 + ROWB : 0u);
-  const rsrc_t rv = make_rsrc((const char*)p.v + voff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * v_ss2 + ROWB : 0u);
-  const rsrc_t ro = make_rsrc((char*)p.o + ooff * 2, (uint32_t)(Lq - 1) * o_ss2 + ROWB);
-
-  // ---- rows: block A = q0 + (lane & 31), block B = A + 32 ----
-  const int q0 = wg_q0 + wave * 64;
-  const int row_a = q0 + (lane & 31), row_b = row_a + 32;
-  u32x4 qa[NDS], qb[NDS];
-#pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    qa[ds] = buf_load16(rq, (uint32_t)row_a * q_ss2 + (2 * ds + hl) * 16);
-    qb[ds] = buf_load16(rq, (uint32_t)row_b * q_ss2 + (2 * ds + hl) * 16);
-  }
-
-  int kv_end = Lk;
-  // causal: row i sees keys j <= i + coff (the mask's diagonal ends at the last query
-  // and the last key; coff = 0 for equal lengths)
-  const int coff = Lk - Lq;
-  if constexpr (CAUSAL) kv_end = max(0, min(Lk, min(Lq, wg_q0 + WG_ROWS) + coff));
-  const int n_tiles = (kv_end + BN - 1) / BN;
-
-  auto issue = [&](const rsrc_t& rsrc, uint32_t ss2, int t, FA_LDS char* dst) {
-    const int k0 = t * BN;
-#pragma unroll
-    for (int i = wave; i < TILE_BYTES / 1024; i += NW) {
-      const int idx = i * 64 + lane;
-      const int r = idx / SLOTS;
-      const int cs = (idx % SLOTS) ^ slot_swizzle<D>(r);
-      buf_load_lds16(rsrc, dst + i * 1024, (uint32_t)(k0 + r) * ss2 + cs * 16);
-    }
-  };
-
-  const int sw_k = slot_swizzle<D>(lane & 15);
-  const int i16 = lane & 15;
-  const int vr1 = 4 * hl + (i16 >> 2);
-  const int sw_v1 = slot_swizzle<D>(vr1), sw_v2 = slot_swizzle<D>(vr1 + 8);
-  const int vc_lo = 2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1);
-  const int vhalf = (i16 & 1) * 8;
-  int off_k[NDS], off_v1[NDB], off_v2[NDB];
-#pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) off_k[ds] = (lane & 31) * ROWB + (((2 * ds + hl) ^ sw_k) << 4);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int cc = 4 * db + vc_lo;
-    off_v1[db] = vr1 * ROWB + ((cc ^ sw_v1) << 4) + vhalf;
-    off_v2[db] = (vr1 + 8) * ROWB + ((cc ^ sw_v2) << 4) + vhalf;
-  }
-
-  RowBlock<NDB> A, B;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) A.o[db] = B.o[db] = f32x16{};
-  A.m_used = B.m_used = -INFINITY;
-  A.mref = B.mref = 0.0f;
-  A.lsum = B.lsum = A.lsum_r = B.lsum_r = 0.0f;
-  const float c = p.scale_log2;
-
-  int n_mine = n_tiles;
-  if constexpr (CAUSAL) n_mine = (q0 + 63 + coff < 0) ? 0 : min(n_tiles, (q0 + 63 + coff) / BN + 1);
-
-  // exponentials of two scores of a block's previous tile -> one packed bf16 pair
-  auto weights2 = [&](const RowBlock<NDB>& X, const f32x16& s, int e, float& acc) -> uint32_t {
-    const float x0 = __builtin_fmaf(s[e], c, -X.mref);
-    const float x1 = __builtin_fmaf(s[e + 1], c, -X.mref);
-    const float p0 = (e % 16 < POLY) ? exp2_poly(x0) : exp2_hw(x0);
-    const float p1 = (e % 16 + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
-    acc += p0;
-    acc += p1;
-    return pack_bf16(p0, p1);
-  };
-  // lazy rescale decision of one block after its row maximum mx (both halves)
-  auto decide = [&](RowBlock<NDB>& X, float mx) {
-    const float m_new = fmaxf(X.m_used, mx);
-    bool need = m_new > X.m_used;
-    if constexpr (TAU > 0) need = need && (X.m_used == -INFINITY || (m_new - X.m_used) * c > (float)TAU);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? (X.m_used == -INFINITY ? 0.0f : exp2_hw((X.m_used - m_new) * c)) : 1.0f;
-      X.m_used = need ? m_new : X.m_used;
-      X.mref = (X.m_used == -INFINITY) ? 0.0f : X.m_used * c;
-      X.lsum *= alpha;
-      X.lsum_r *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) X.o[db][r] *= alpha;
-    }
-  };
-
-  // one pipelined step j (see fwd_kernel): phase 1 = S(j) for both blocks with the
-  // weights of tile j-1; phase 2 = PV(j-1) for both blocks with the maxima of S(j)
-  auto step = [&](const int j, auto par_c, auto prev_c, auto next_c, auto mask_c, f32x16(&sa_prev)[NKB],
-                  f32x16(&sb_prev)[NKB], f32x16(&sa_next)[NKB], f32x16(&sb_next)[NKB]) {
-    constexpr int PAR = decltype(par_c)::value;
-    constexpr bool PREV = decltype(prev_c)::value;
-    constexpr bool NEXT = decltype(next_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(PAR ^ 1));
-    if (j < n_tiles) issue(rv, v_ss2, j, vbuf(PAR));
-    const FA_LDS char* kt = kbuf(PAR);
-    const FA_LDS char* vt = vbuf(PAR ^ 1);
-    const int k0 = j * BN;
-
-    // -- phase 1 --
-    constexpr int UPD = 8 / NDS;  // score pairs per block per K fragment
-    u32x4 pa[2 * NKB], pbb[2 * NKB];
-    float rsa[2] = {0.0f, 0.0f}, rsb[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      if constexpr (NEXT) sa_next[kb] = sb_next[kb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        u32x4 a{};
-        if constexpr (NEXT) {
-          a = lds_read16(kt + 32 * kb * ROWB + off_k[ds]);
-          sa_next[kb] = mfma_bf16(a, qa[ds], sa_next[kb]);
-        }
-        if constexpr (PREV) {
-#pragma unroll
-          for (int uu = 0; uu < UPD; ++uu) {
-            const int u = ds * UPD + uu;
-            pbb[2 * kb + (u >> 2)][u & 3] = weights2(B, sb_prev[kb], 2 * u, rsb[u & 1]);
-          }
-        }
-        if constexpr (NEXT) sb_next[kb] = mfma_bf16(a, qb[ds], sb_next[kb]);
-        if constexpr (PREV) {
-#pragma unroll
-          for (int uu = 0; uu < UPD; ++uu) {
-            const int u = ds * UPD + uu;
-            pa[2 * kb + (u >> 2)][u & 3] = weights2(A, sa_prev[kb], 2 * u, rsa[u & 1]);
-          }
-        }
-      }
-      if constexpr (NEXT && PREV) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5 * UPD, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5 * UPD, 0);
-          if (ds < NDS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-    }
-    if constexpr (PREV) {
-      A.lsum += rsa[0] + rsa[1];
-      B.lsum += rsb[0] + rsb[1];
-    }
-    if constexpr (NEXT && MASK) {
-      int lim_a = Lk, lim_b = Lk;
-      if constexpr (CAUSAL) {
-        lim_a = min(lim_a, row_a + 1 + coff);
-        lim_b = min(lim_b, row_b + 1 + coff);
-      }
-      lim_a -= k0 + 4 * hl;
-      lim_b -= k0 + 4 * hl;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = 32 * kb + 8 * (r >> 2) + (r & 3);
-          sa_next[kb][r] = rel >= lim_a ? -INFINITY : sa_next[kb][r];
-          sb_next[kb][r] = rel >= lim_b ? -INFINITY : sb_next[kb][r];
-        }
-    }
-
-    // -- phase 2 --
-    float mxa = -INFINITY, mxb = -INFINITY;
-    if constexpr (PREV) {
-      float rra[2] = {0.0f, 0.0f}, rrb[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int g = 0; g < BN / 16; ++g) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
-          const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
-          const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          A.o[db] = mfma_bf16(va, pa[g], A.o[db]);
-#pragma unroll
-          for (int e = db * 4 / NDB; e < (db + 1) * 4 / NDB; ++e) rra[e & 1] = add_bf16_pair(pa[g][e], rra[e & 1]);
-          if constexpr (NEXT) {
-            const int i = g * NDB + db;
-#pragma unroll
-            for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
-              mxa = max3(mxa, sa_next[q >> 4][q & 15], sa_next[q >> 4][(q & 15) + 1]);
-          }
-          B.o[db] = mfma_bf16(va, pbb[g], B.o[db]);
-#pragma unroll
-          for (int e = db * 4 / NDB; e < (db + 1) * 4 / NDB; ++e) rrb[e & 1] = add_bf16_pair(pbb[g][e], rrb[e & 1]);
-          if constexpr (NEXT) {
-            const int i = g * NDB + db;
-#pragma unroll
-            for (int q = i * 32 / (BN / 16 * NDB); q < (i + 1) * 32 / (BN / 16 * NDB); q += 2)
-              mxb = max3(mxb, sb_next[q >> 4][q & 15], sb_next[q >> 4][(q & 15) + 1]);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < BN / 16 * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        if (i < BN / 16 * NDB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      A.lsum_r += rra[0] + rra[1];
-      B.lsum_r += rrb[0] + rrb[1];
-    } else if constexpr (NEXT) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          mxa = __builtin_fmaxf(mxa, sa_next[kb][r]);
-          mxb = __builtin_fmaxf(mxb, sb_next[kb][r]);
-        }
-    }
-    if constexpr (NEXT) {
-      decide(A, half_swap_max(mxa));
-      decide(B, half_swap_max(mxb));
-    }
-  };
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using BF = std::false_type;
-  using BT = std::true_type;
-  int j_plain = Lk / BN;
-  if constexpr (CAUSAL) j_plain = min(j_plain, max(0, q0 + 1 + coff) / BN);
-  const int j_lim = min(n_mine, j_plain);
-  f32x16 sa0[NKB], sa1[NKB], sb0[NKB], sb1[NKB];
-  if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
-  int j = 0;
-  if (n_mine > 0) {
-    step(0, I0{}, BF{}, BT{}, BT{}, sa1, sb1, sa0, sb0);
-    j = 1;
-    for (; j + 1 < j_lim; j += 2) {  // j odd
-      step(j, I1{}, BT{}, BT{}, BF{}, sa0, sb0, sa1, sb1);
-      step(j + 1, I0{}, BT{}, BT{}, BF{}, sa1, sb1, sa0, sb0);
-    }
-    for (; j + 1 < n_mine; j += 2) {
-      step(j, I1{}, BT{}, BT{}, BT{}, sa0, sb0, sa1, sb1);
-      step(j + 1, I0{}, BT{}, BT{}, BT{}, sa1, sb1, sa0, sb0);
-    }
-    if (j < n_mine) {
-      step(j, I1{}, BT{}, BT{}, BT{}, sa0, sb0, sa1, sb1);
-      step(j + 1, I0{}, BT{}, BF{}, BF{}, sa1, sb1, sa0, sb0);
-      j += 2;
-    } else {
-      step(j, I1{}, BT{}, BF{}, BF{}, sa0, sb0, sa1, sb1);
-      j += 1;
-    }
-  }
-  for (; j <= n_tiles; ++j) {
-    wait_vmem();
-    __syncthreads();
-    const int par = j & 1;
-    if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(par ^ 1));
-    if (j < n_tiles) issue(rv, v_ss2, j, vbuf(par));
-  }
-
-  // ---- epilogue ----
-  auto finish = [&](const RowBlock<NDB>& X, int row) {
-    const float lt = half_swap_sum(X.lsum);
-    const float ltr = half_swap_sum(X.lsum_r);
-    const float inv = ltr > 0.0f ? 1.0f / ltr : 0.0f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * hl;
-        const u32x2 w = {pack_bf16(X.o[db][4 * q4 + 0] * inv, X.o[db][4 * q4 + 1] * inv),
-                         pack_bf16(X.o[db][4 * q4 + 2] * inv, X.o[db][4 * q4 + 3] * inv)};
-        buf_store8(ro, (uint32_t)row * o_ss2 + d * 2, w);
-      }
-    if (hl == 0 && row < Lq) {
-      float lse = -INFINITY;
-      if (lt > 0.0f) lse = (X.m_used * c + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
-      p.lse[lseoff + row] = lse;
-    }
-  };
-  finish(A, row_a);
-  finish(B, row_b);
-}
-
 // ---- merge of the key chunks' partial results ----
 // One thread per (head, query row, 4 columns of O): LSE = m + ln sum_c e^(LSE_c - m)
 // with m = max_c LSE_c, and O = sum_c e^(LSE_c - LSE) O_c, in chunk order.  Chunks
@@ -902,7 +536,7 @@ hipError_t launch_fwd_schedule(const int32_t* cu_q, const int32_t* cu_k, int bat
 }
 
 template <int D, int NQT, bool CAUSAL, bool VARLEN, int POLY, int TAU>
-static hipError_t launch_one(const FwdParams& p, hipStream_t stream, int max_items, int rows_per_wave) {
+static hipError_t launch_one(const FwdParams& p, hipStream_t stream, int max_items) {
   const int items = VARLEN ? max_items : p.n_qtiles * p.batch;
   const unsigned grid = (unsigned)items * (unsigned)p.heads;
   if (grid == 0) return hipSuccess;
@@ -918,26 +552,19 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream, int max_ite
       return hipGetLastError();
     }
   }
-  if constexpr (NQT == 2) {
-    if (rows_per_wave == 64) {
-      hipLaunchKernelGGL((fwd64_kernel<D, CAUSAL, VARLEN, POLY, TAU>), dim3(grid), dim3(256), 0, stream, p);
-      return hipGetLastError();
-    }
-  }
   hipLaunchKernelGGL((fwd_kernel<D, NQT, CAUSAL, VARLEN, POLY, TAU>), dim3(grid), dim3(256 * NQT), 0, stream, p);
   return hipGetLastError();
 }
 
+// The exp2 split shares 2 and 4 and the eager threshold (tau = 0) are measurement
+// variants: compiled for head_dim 128 and fixed-length batches only.
 template <int D, int NQT, bool CAUSAL, bool VARLEN>
 static hipError_t dispatch_poly_tau(const FwdParams& p, const FwdConfig& cfg, hipStream_t s, int mi) {
-  if (cfg.tau == 8) {
-    switch (cfg.poly_per16) {
-      case 0: return launch_one<D, NQT, CAUSAL, VARLEN, 0, 8>(p, s, mi, cfg.rows_per_wave);
-      case 2: return launch_one<D, NQT, CAUSAL, VARLEN, 2, 8>(p, s, mi, cfg.rows_per_wave);
-      case 4: return launch_one<D, NQT, CAUSAL, VARLEN, 4, 8>(p, s, mi, cfg.rows_per_wave);
-    }
-  } else if (cfg.tau == 0 && cfg.poly_per16 == 0) {
-    return launch_one<D, NQT, CAUSAL, VARLEN, 0, 0>(p, s, mi, cfg.rows_per_wave);
+  if (cfg.tau == 8 && cfg.poly_per16 == 0) return launch_one<D, NQT, CAUSAL, VARLEN, 0, 8>(p, s, mi);
+  if constexpr (D == 128 && !VARLEN) {
+    if (cfg.tau == 8 && cfg.poly_per16 == 2) return launch_one<D, NQT, CAUSAL, VARLEN, 2, 8>(p, s, mi);
+    if (cfg.tau == 8 && cfg.poly_per16 == 4) return launch_one<D, NQT, CAUSAL, VARLEN, 4, 8>(p, s, mi);
+    if (cfg.tau == 0 && cfg.poly_per16 == 0) return launch_one<D, NQT, CAUSAL, VARLEN, 0, 0>(p, s, mi);
   }
   return hipErrorInvalidValue;
 }

@@ -48,8 +48,7 @@ struct FwdConfig {
   bool varlen;
   int poly_per16;   // 0, 2, 4
   int tau;          // 8 or 0
-  int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd64_kernel, q_tiles == 2)
-  int key_splits;     // 1, or > 1 for the split forward (q_tiles == 1, 32 rows per wave) + merge
+  int key_splits;     // 1, or > 1 for the split forward (q_tiles == 1) + merge
 };
 
 // Returns hipSuccess or the launch error.  Grid size is derived from p and cfg.
