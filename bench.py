@@ -113,12 +113,15 @@ def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
         lens = [int(x) for x in inp.seqlens()]
         f_fwd = W.fwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal)
         f_bwd = W.bwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal)
-        o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx)
+        ws_f = FA.fwd_workspace(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx)
+        o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx, workspace=ws_f)
         dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in (q, k, v))
+        ws_b = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         run = {"fwd": lambda: FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx,
-                                     out=o, lse=lse),
+                                     out=o, lse=lse, workspace=ws_f),
                "bwd": lambda: FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, cu_seqlens_q=cu,
-                                     max_seqlen_q=mx, deterministic=deterministic, dq=dq, dk=dk, dv=dv)}
+                                     max_seqlen_q=mx, deterministic=deterministic, dq=dq, dk=dk, dv=dv,
+                                     workspace=ws_b)}
         row = {}
         # the 4096-token workloads (K+V 128 MiB) fit in the 256 MB last-level cache: time
         # them also with a 512 MiB scratch write between calls (outside the timed region)
@@ -144,7 +147,7 @@ def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
                     "tflops_max": round(flop / (ms.min() * 1e-3) / 1e12, 2)}
         res[name] = row
         del flush
-        del q, k, v, do, o, lse, dq, dk, dv
+        del q, k, v, do, o, lse, dq, dk, dv, ws_f, ws_b
         torch.cuda.empty_cache()
     return res
 
@@ -171,7 +174,7 @@ def time_decode(warmup: int = 10, iters: int = 50):
         row = {}
         for label, splits in (("auto_split", -1), ("no_split", 1)):
             t = FA.Tuning(key_splits=splits)
-            ws = torch.empty(1 << 26, dtype=torch.uint8, device="cuda")
+            ws = FA.fwd_workspace(q, k, v, 1.0 / D ** 0.5, True, tuning=t)
             fn = lambda: FA.fwd(q, k, v, 1.0 / D ** 0.5, True, tuning=t, out=o, lse=lse, workspace=ws)
             for _ in range(warmup):
                 fn()
@@ -232,10 +235,11 @@ def main():
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
     ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")   # >= either mode's workspace (fp32 dQ accumulator)
     tuning = FA.Tuning(args.poly, args.tau, args.q_tiles)
+    ws_f = FA.fwd_workspace(q, k, v, inp.scale, True, tuning=tuning)  # the fp16 copy of V
     det = not args.atomic
 
     def fwd():
-        FA.fwd(q, k, v, inp.scale, True, tuning=tuning, out=o, lse=lse)
+        FA.fwd(q, k, v, inp.scale, True, tuning=tuning, out=o, lse=lse, workspace=ws_f)
 
     def bwd(phases=L.FA_BWD_PHASE_ALL):
         FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=det, dq=dq, dk=dk, dv=dv, workspace=ws,

@@ -125,8 +125,11 @@ typedef struct fa_fwd_tuning {
 
 /* Bytes of device workspace fa_fwd needs for `a` and `tuning` (NULL = defaults):
  * room for the longest-first work list of variable-length batches (fdeinterviews.com
- * FA4 summary, features paragraph) and for the partial results of a key split; 0
- * when neither is used.  Validates `a` and `tuning` exactly as fa_fwd does and
+ * FA4 summary, features paragraph), for the partial results of a key split, and for
+ * an fp16 copy of V with one power-of-two exponent per 64-key tile (2 bytes per V
+ * element plus 4 bytes per key row and head): the PV product runs in fp16, so that
+ * the weights keep 11 significant bits under the lazy reference.  0 only for an
+ * empty problem.  Validates `a` and `tuning` exactly as fa_fwd does and
  * returns the same status; `bytes` must not be NULL (FA_ERR_INVALID_ARGUMENT).  No
  * HIP call is made. */
 fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tuning, size_t* bytes);
@@ -149,7 +152,9 @@ fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tunin
  *                            longer than 524,288, a tuning without an instance;
  *   FA_ERR_WORKSPACE_TOO_SMALL  workspace NULL or smaller than required;
  *   FA_ERR_HIP               a kernel launch failed.
- * An empty batch (batch = 0 or no query rows) returns FA_OK with no work. */
+ * An empty batch (batch = 0 or no query rows) returns FA_OK with no work.
+ * V elements must be below 2^31 in magnitude (the fp16 copy's exponent range);
+ * max_seqlen_k must bound every key length (it sizes the copy's grid). */
 fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* workspace,
                  size_t workspace_bytes, void* stream);
 

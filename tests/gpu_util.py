@@ -143,6 +143,31 @@ def _oracle_bwd_head(inp: I.AttnInputs, b: int, h: int, o_bf16: bool):
     return OA.head_backward(q, k, v, do, inp.scale, inp.causal, o=o)
 
 
+def oracle_forward_tensors(inp: I.AttnInputs):
+    """The oracle's forward output for every (sequence, head), laid out as the library
+    lays out its own: O rounded to bf16 (RNE) in the input layout and LSE as fp32
+    ([B, H, S] or [H, T]).  Fed to the backward in place of the GPU forward's O and
+    LSE, it gives the backward exactly the inputs the o_bf16 oracle assumes, so the
+    comparison measures the backward alone."""
+    o = np.zeros(inp.q.shape, dtype=np.uint16)
+    if inp.varlen:
+        lse = np.full((inp.num_heads, inp.q.shape[0]), -np.inf, dtype=np.float32)
+    else:
+        lse = np.full((inp.batch, inp.num_heads, inp.q.shape[1]), -np.inf, dtype=np.float32)
+    pairs = [(b, h) for b in range(inp.batch) for h in range(inp.num_heads)]
+    res = oracle_map(lambda bh: oracle_fwd_head(inp, bh[0], bh[1]), pairs)
+    for (b, h), (ro, rl) in zip(pairs, res):
+        bits = I.f32_to_bf16_bits(ro.astype(np.float32))
+        if inp.varlen:
+            s0, s1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+            o[s0:s1, h] = bits
+            lse[h, s0:s1] = rl.astype(np.float32)
+        else:
+            o[b, :, h] = bits
+            lse[b, h] = rl.astype(np.float32)
+    return dev_bf16(o), torch.from_numpy(lse).cuda()
+
+
 def gpu_head(t: torch.Tensor, inp: I.AttnInputs, b: int, h: int, kind: str = "q") -> np.ndarray:
     """[L, D] slice of a GPU output tensor (same layout as the inputs), as float64 numpy.
     kind "k" slices key-shaped tensors (dK, dV) by the key offsets."""

@@ -60,8 +60,21 @@ def fwd_status(a, tuning=None, ws=None, ws_bytes=0):
     return L.lib().fa_fwd(ctypes.byref(a), ctypes.byref(t), ws, ws_bytes, None)
 
 
-def test_fixed_length_forward_needs_no_workspace():
-    assert ws_size(fwd_args()) == (L.FA_OK, 0)
+def v16_bytes(h, total_k, d):
+    """Workspace of the fp16 copy of V and its per-tile exponents (256-byte aligned parts)."""
+    r = lambda x: (x + 255) // 256 * 256
+    return r(h * total_k * d * 2) + r(h * total_k * 4)
+
+
+def test_fixed_length_forward_workspace_is_the_fp16_v_copy():
+    # the PV product runs in fp16: the workspace holds V converted to fp16 (2 bytes per
+    # element) and one int32 exponent slot per key row and head
+    assert ws_size(fwd_args()) == (L.FA_OK, v16_bytes(4, 2 * 256, 128))
+    assert ws_size(fwd_args(d=64)) == (L.FA_OK, v16_bytes(4, 2 * 256, 64))
+    assert fwd_status(fwd_args(), ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    assert fwd_status(fwd_args(), ws=P, ws_bytes=v16_bytes(4, 512, 128) - 1) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    empty = fwd_args(b=0)
+    assert ws_size(empty) == (L.FA_OK, 0)
 
 
 @pytest.mark.parametrize("mutate,expect", [
@@ -192,23 +205,24 @@ def test_backward_workspace_sizes():
 def test_key_split_workspace_and_validation():
     a = fwd_args(b=2, s=256, h=4, d=128)
     a.seqlen_q, a.seqlen_k = 8, 16384
-    assert ws_size(a, L.FwdTuning(-1, -1, -1, 1)) == (L.FA_OK, 0)              # split off: no workspace
+    base = v16_bytes(4, 2 * 16384, 128)
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, 1)) == (L.FA_OK, base)           # split off: the V copy only
     st, n = ws_size(a, L.FwdTuning(-1, -1, -1, 4))
     rows = 4 * 4 * 2 * 8                                                   # splits * heads * total_q
-    assert st == L.FA_OK and n >= rows * 4 + rows * 128 * 4 and n % 256 == 0
+    assert st == L.FA_OK and n >= base + rows * 4 + rows * 128 * 4 and n % 256 == 0
     st, n_auto = ws_size(a)                                                # 8 work items: split chosen
-    assert st == L.FA_OK and n_auto > 0
+    assert st == L.FA_OK and n_auto > base
     assert ws_size(a, L.FwdTuning(-1, -1, -1, 65))[0] == L.FA_ERR_UNSUPPORTED
     assert fwd_status(a, L.FwdTuning(-1, -1, -1, 4), ws=None, ws_bytes=0) == L.FA_ERR_WORKSPACE_TOO_SMALL
     big = fwd_args()                                                       # many work items: no split
-    assert ws_size(big) == (L.FA_OK, 0)
+    assert ws_size(big) == (L.FA_OK, v16_bytes(4, 512, 128))
 
 
 def test_causal_with_unequal_lengths_is_accepted():
     # the causal mask aligns the diagonal to the bottom-right corner, so L_q != L_k is valid
     a = fwd_args()
     a.causal, a.seqlen_k = 1, 1000
-    assert ws_size(a) == (L.FA_OK, 0)
+    assert ws_size(a) == (L.FA_OK, v16_bytes(4, 2 * 1000, 128))
     b = bwd_args()
     b.seqlen_k = 100
     assert bwd_ws(b)[0] == L.FA_OK

@@ -6,12 +6,27 @@ import torch
 
 from tiled_exact_attention_bf16_amd import inputs as I
 from tests.gpu_util import (TOL_MAX, TOL_MEAN, bf16_rounding_floor, bf16_rounding_max, errors, gpu_head,
-                            named_inputs, oracle_bwd_head, oracle_map, say, upload)
+                            named_inputs, oracle_bwd_head, oracle_forward_tensors, oracle_map, say, upload)
 
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from tiled_exact_attention_bf16_amd import attention as FA
+
+
+def run_bwd_on_oracle_forward(inp, deterministic, grad_dtype=torch.float32, cu_k=None):
+    """The backward alone: O (bf16) and LSE (fp32) come from the oracle's forward."""
+    q, k, v, do, cu = upload(inp)
+    o, lse = oracle_forward_tensors(inp)
+    kw = {}
+    if inp.varlen:
+        kw = dict(cu_seqlens_q=cu, max_seqlen_q=inp.max_seqlen())
+        if cu_k is not None:
+            kw.update(cu_seqlens_k=cu_k, max_seqlen_k=inp.max_seqlen_k())
+    dq, dk, dv = FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, deterministic=deterministic,
+                        grad_dtype=grad_dtype, **kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv
 
 
 def run_fwd_bwd(inp, deterministic, grad_dtype=torch.float32):
@@ -25,14 +40,14 @@ def run_fwd_bwd(inp, deterministic, grad_dtype=torch.float32):
 
 
 def check_grads(inp, grads, pairs, tag, strict=False, cache_key=None):
-    """strict (the named workloads): the exact fp64 oracle at the literal bar.
+    """strict (the named workloads, run end to end from the GPU forward): the exact fp64
+    oracle at the literal bar.
 
-    Otherwise (edge-case shapes: a handful of keys per row, so large weights and
-    large gradients): the oracle whose row terms D_i = dO_i . O_i use the oracle's own
-    O rounded to bf16 -- the forward output exactly as the backward receives it (it
-    reads the stored bf16 O) -- again at the literal bar.  bf16 gradient outputs also
-    carry their own rounding (no bf16 output can beat bf16 of the oracle), which is
-    added to the bar."""
+    Otherwise (edge-case shapes: a handful of keys per row, so large weights and large
+    gradients; run by run_bwd_on_oracle_forward): the oracle whose row terms
+    D_i = dO_i . O_i use the oracle's own O rounded to bf16 -- the O that backward was
+    handed -- again at the literal bar.  bf16 gradient outputs also carry their own
+    rounding (no bf16 output can beat bf16 of the oracle), which is added to the bar."""
     worst = {}
     refs = oracle_map(lambda bh: oracle_bwd_head(inp, bh[0], bh[1], o_bf16=not strict, cache_key=cache_key), pairs)
     for (b, h), ref in zip(pairs, refs):
@@ -56,7 +71,7 @@ def check_grads(inp, grads, pairs, tag, strict=False, cache_key=None):
 def test_small_shapes(s, causal, d, deterministic):
     inp = I.random_inputs(200 + s, 2, s, 2, d, causal, with_do=True)
     say(f"case s={s} causal={causal} d={d} det={deterministic}")
-    grads = run_fwd_bwd(inp, deterministic)
+    grads = run_bwd_on_oracle_forward(inp, deterministic)
     check_grads(inp, grads, [(b, h) for b in range(2) for h in range(2)], f"s{s}c{int(causal)}d{d}det{int(deterministic)}")
 
 
@@ -66,7 +81,7 @@ def test_causal_unequal_lengths(lq, lk, deterministic):
     # bottom-right causal alignment; with lq > lk the first lq - lk rows see no key
     inp = I.random_inputs(400 + lq + lk, 2, lq, 2, 128, True, with_do=True, seqlen_k=lk)
     say(f"case causal lq={lq} lk={lk} det={deterministic}")
-    grads = run_fwd_bwd(inp, deterministic)
+    grads = run_bwd_on_oracle_forward(inp, deterministic)
     check_grads(inp, grads, [(b, h) for b in range(2) for h in range(2)], f"causal{lq}x{lk}det{int(deterministic)}")
 
 
@@ -79,12 +94,7 @@ def test_varlen_separate_key_lengths(causal, deterministic):
     rng = np.random.default_rng(79)
     inp.do = I.f32_to_bf16_bits(rng.standard_normal(inp.q.shape, dtype=np.float32))
     say(f"case varlen q/k lengths causal={causal} det={deterministic}")
-    q, k, v, do, cu = upload(inp)
-    cu_k = torch.from_numpy(inp.cu_seqlens_k).cuda()
-    kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu_k, max_seqlen_q=inp.max_seqlen(), max_seqlen_k=inp.max_seqlen_k())
-    o, lse = FA.fwd(q, k, v, inp.scale, causal, **kw)
-    grads = FA.bwd(do, q, k, v, o, lse, inp.scale, causal, deterministic=deterministic, **kw)
-    torch.cuda.synchronize()
+    grads = run_bwd_on_oracle_forward(inp, deterministic, cu_k=torch.from_numpy(inp.cu_seqlens_k).cuda())
     check_grads(inp, grads, [(b, h) for b in range(len(q_lens)) for h in range(2)],
                 f"varlenqk c{int(causal)}det{int(deterministic)}")
 
@@ -94,13 +104,13 @@ def test_varlen_ragged(deterministic):
     lens = [0, 1, 5, 128, 129, 300, 17, 0, 256, 511]
     inp = I.random_varlen_inputs(12, lens, heads=2, head_dim=128, causal=True, with_do=True)
     say(f"case varlen det={deterministic}")
-    grads = run_fwd_bwd(inp, deterministic)
+    grads = run_bwd_on_oracle_forward(inp, deterministic)
     check_grads(inp, grads, [(b, h) for b in range(len(lens)) for h in range(2)], f"varlen det{int(deterministic)}")
 
 
 def test_bf16_gradient_outputs():
     inp = I.random_inputs(300, 1, 512, 2, 128, True, with_do=True)
-    grads = run_fwd_bwd(inp, False, grad_dtype=torch.bfloat16)
+    grads = run_bwd_on_oracle_forward(inp, False, grad_dtype=torch.bfloat16)
     assert all(g.dtype == torch.bfloat16 for g in grads)
     check_grads(inp, grads, [(0, 0), (0, 1)], "bf16-out")
 
@@ -136,10 +146,10 @@ def test_canaries_and_strided_views(deterministic, grad_dtype):
 
     qv, kv, vv, dov = widened(q), widened(k), widened(v), widened(do)
     assert not qv.is_contiguous()
+    o_ref, lse = oracle_forward_tensors(inp)
     o_big = torch.full((B, S, H + 1, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     o = o_big[:, :, 1:]
-    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    FA.fwd(qv, kv, vv, inp.scale, True, out=o, lse=lse)
+    o.copy_(o_ref)
     nan = float("nan")
     bigs = [torch.full((B * S * (H + 1) * D + 4096,), nan, dtype=grad_dtype, device="cuda") for _ in range(3)]
     views = [t[: B * S * (H + 1) * D].view(B, S, H + 1, D)[:, :, 1:] for t in bigs]
@@ -151,7 +161,7 @@ def test_canaries_and_strided_views(deterministic, grad_dtype):
         body = big[: B * S * (H + 1) * D].view(B, S, H + 1, D)
         assert bool(torch.isnan(body[:, :, 0]).all()), f"{name}: write into the skipped head"
         assert bool(torch.isnan(big[B * S * (H + 1) * D:]).all()), f"{name}: write past the buffer"
-    assert bool(torch.isnan(o_big[:, :, 0]).all()), "O: write into the skipped head"
+    assert bool(torch.isnan(o_big[:, :, 0]).all()), "the backward wrote into O's skipped head"
     check_grads(inp, (dq, dk, dv), [(b, h) for b in range(B) for h in range(H)],
                 f"canaries det{int(deterministic)} {str(grad_dtype)[6:]}")
 

@@ -183,6 +183,22 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Option
     return out, lse
 
 
+def fwd_workspace(q, k, v, softmax_scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=None,
+                  max_seqlen_q=None, max_seqlen_k=None, tuning: Optional[Tuning] = None) -> Optional[torch.Tensor]:
+    """A device workspace of the size fa_fwd needs for these arguments (None if 0 bytes),
+    for callers that reuse one across calls."""
+    _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    varlen = cu_seqlens_q is not None
+    a = fwd_args(q, k, v, q, q, softmax_scale, causal, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    t = (tuning or Tuning()).c()
+    need = ctypes.c_size_t(0)
+    L.check(L.lib().fa_fwd_workspace_size(ctypes.byref(a), ctypes.byref(t), ctypes.byref(need)),
+            "fa_fwd_workspace_size")
+    return torch.empty(need.value, dtype=torch.uint8, device=q.device) if need.value else None
+
+
 def build_schedule(q, k, cu_seqlens, causal, max_seqlen=None, tuning: Optional[Tuning] = None, stream=None):
     """Runs only the variable-length longest-first list builder; returns (tile_rows, [(seq, tile), ...])."""
     _check_qkv(q, k, k, cu_seqlens, None)

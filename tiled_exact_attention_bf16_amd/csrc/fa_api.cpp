@@ -69,6 +69,7 @@ fa_status check_shape(int batch, int seqlen_q, int seqlen_k, int heads, int d, c
     s.total_k = batch * seqlen_k;
   }
   if ((s.max_q + 63) / 64 > fa::kSchedMaxCost || (s.max_k + 63) / 64 > fa::kSchedMaxCost) return FA_ERR_UNSUPPORTED;
+  if (batch > 65535 || heads > 65535) return FA_ERR_UNSUPPORTED;  // grid dimensions of per-sequence kernels
   s.cu_q = cu_q;
   s.cu_k = cu_k;
   *out = s;
@@ -150,8 +151,9 @@ int fwd_key_splits(const Shape& s, const FwdChoice& c) {
 }
 
 // Forward workspace: [work list (variable length)] [partial LSE] [partial O]
+// [fp16 copy of V: H x total_k x D] [per-tile exponents of the copy: H x total_k int32]
 struct FwdWs {
-  size_t lse_off, o_off, total;
+  size_t lse_off, o_off, v16_off, vexp_off, total;
 };
 
 FwdWs fwd_ws_layout(const Shape& s, int tile_rows, int splits) {
@@ -164,6 +166,11 @@ FwdWs fwd_ws_layout(const Shape& s, int tile_rows, int splits) {
     w.o_off = off;
     off += round_up(rows * s.d * sizeof(float));
   }
+  const size_t krows = (size_t)s.heads * s.total_k;
+  w.v16_off = off;
+  off += round_up(krows * s.d * sizeof(uint16_t));
+  w.vexp_off = off;
+  off += round_up(krows * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -186,6 +193,7 @@ fa::FwdParams make_fwd_params(const fa_fwd_args* a, const Shape& s) {
   p.cu_q = s.cu_q;
   p.cu_k = s.cu_k;
   p.total_q = s.total_q;
+  p.total_k = s.total_k;
   p.scale = a->softmax_scale;
   p.scale_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
   p.n_split = 1;
@@ -277,6 +285,8 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
     p.part_lse = (float*)((char*)workspace + ws.lse_off);
     p.part_o = (float*)((char*)workspace + ws.o_off);
   }
+  p.v16 = (uint16_t*)((char*)workspace + ws.v16_off);
+  p.v_exp = (int32_t*)((char*)workspace + ws.vexp_off);
   fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, splits};
   hipStream_t strm = (hipStream_t)stream;
   if (s.varlen) {
@@ -284,6 +294,7 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
                                            (int32_t*)workspace, strm);
     if (e != hipSuccess) return FA_ERR_HIP;
   }
+  if (s.total_k > 0 && fa::launch_fwd_vprep(p, s.d, s.varlen, strm) != hipSuccess) return FA_ERR_HIP;
   return fa::launch_fwd(p, cfg, strm) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

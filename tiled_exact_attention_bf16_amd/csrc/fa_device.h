@@ -24,6 +24,8 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -74,6 +76,12 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Same tile shapes and k mapping with fp16 operands (v_mfma_f32_32x32x16_f16).
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
 __device__ __forceinline__ u32x2 lds_read_tr16(const FA_LDS char* p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)p);
   return __builtin_bit_cast(u32x2, r);
@@ -89,6 +97,18 @@ __device__ __forceinline__ void lds_write16(FA_LDS char* p, u32x4 v) { *(FA_LDS 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Round-to-nearest-even narrowing of two floats into one packed fp16 pair.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a packed fp16 pair, in one v_dot2 instruction (products by 1.0 are exact).
+__device__ __forceinline__ float add_f16_pair(uint32_t w, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
 }
 
 // acc + lo + hi of a packed bf16 pair, in one v_dot2 instruction (products by 1.0 are exact).

@@ -22,7 +22,13 @@
 //     double buffer (the next tile streams in while the current one is used), with
 //     an XOR swizzle that keeps the operand reads bank-conflict free;
 //   * P goes from the S^T accumulators straight into the B operand of
-//     O^T = V^T P^T; V^T comes from ds_read_b64_tr_b16 transpose reads;
+//     O^T = V^T P^T, rounded to fp16: with the lazy reference a row's largest
+//     weights sit up to 2^8 above it, and bf16's 8 significant bits then leave an
+//     error near 1e-2 on outputs of magnitude 2-4, where fp16's 11 bits do not.  V is
+//     read from an fp16 copy made by vprep_kernel, each 64-key tile scaled by a
+//     power of two 2^-e so that the copy is exact; the tile's weights carry the
+//     factor 2^e back (it is folded into the exponent argument), so P'V' = PV;
+//     V^T comes from ds_read_b64_tr_b16 transpose reads;
 //   * the O^T accumulators also hold one query row per lane, so the rescale factor
 //     is a per-lane scalar.
 #include <type_traits>
@@ -77,22 +83,23 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     h = bh - b * p.heads;
   }
   int Lq = p.seqlen_q, Lk = p.seqlen_k;
-  int64_t qoff, koff, voff, ooff, lseoff;
+  int64_t qoff, koff, ooff, lseoff;
+  int64_t krow0;  // first key row of the sequence among all key rows (the fp16 V copy's rows)
   if constexpr (VARLEN) {
     const int sq = p.cu_q[b], sk = p.cu_k[b];
     Lq = p.cu_q[b + 1] - sq;
     Lk = p.cu_k[b + 1] - sk;
     qoff = sq * p.q_ss + h * p.q_sh;
     koff = sk * p.k_ss + h * p.k_sh;
-    voff = sk * p.v_ss + h * p.v_sh;
     ooff = sq * p.o_ss + h * p.o_sh;
     lseoff = (int64_t)h * p.total_q + sq;
+    krow0 = sk;
   } else {
     qoff = b * p.q_sb + h * p.q_sh;
     koff = b * p.k_sb + h * p.k_sh;
-    voff = b * p.v_sb + h * p.v_sh;
     ooff = b * p.o_sb + h * p.o_sh;
     lseoff = ((int64_t)b * p.heads + h) * Lq;
+    krow0 = (int64_t)b * Lk;
   }
   const int wg_q0 = qtile * WG_ROWS;
   if (wg_q0 >= Lq) return;
@@ -107,16 +114,19 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const int per = (tiles + p.n_split - 1) / p.n_split;
     const int kbase = min(chunk * per, tiles) * kFwdBlockN;
     koff += (int64_t)kbase * p.k_ss;
-    voff += (int64_t)kbase * p.v_ss;
+    krow0 += kbase;
     Lk = max(0, min(Lk - kbase, per * kFwdBlockN));
     coff -= kbase;
   }
 
   const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), k_ss2 = (uint32_t)(p.k_ss * 2);
-  const uint32_t v_ss2 = (uint32_t)(p.v_ss * 2), o_ss2 = (uint32_t)(p.o_ss * 2);
+  const uint32_t v_ss2 = (uint32_t)ROWB, o_ss2 = (uint32_t)(p.o_ss * 2);
   const rsrc_t rq = make_rsrc((const char*)p.q + qoff * 2, (uint32_t)(Lq - 1) * q_ss2 + ROWB);
   const rsrc_t rk = make_rsrc((const char*)p.k + koff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * k_ss2 + ROWB : 0u);
-  const rsrc_t rv = make_rsrc((const char*)p.v + voff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * v_ss2 + ROWB : 0u);
+  // the fp16 copy of V: rows of this (sequence, head) are contiguous, ROWB bytes apart
+  const int64_t vrow = (int64_t)h * p.total_k + krow0;
+  const rsrc_t rv = make_rsrc(p.v16 + vrow * D, Lk > 0 ? (uint32_t)Lk * ROWB : 0u);
+  const int32_t* v_exp = p.v_exp + vrow;  // tile j's exponent at v_exp[j * BN]
   const rsrc_t ro = make_rsrc((char*)p.o + ooff * 2, (uint32_t)(Lq - 1) * o_ss2 + ROWB);
 
   // ---- rows of this wave; Q as B operand (lane: row, 8 consecutive d) ----
@@ -165,8 +175,10 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_used = -INFINITY;
   float mref = 0.0f;    // m_used * c once a row has seen a key
+  float mref_x = 0.0f;  // mref - e of the tile whose weights are formed next (weights carry 2^e)
+  float esc = 1.0f;     // 2^-e of that tile: its weight sums back in true units
   float lsum = 0.0f;    // sum of fp32 weights
-  float lsum_r = 0.0f;  // sum of bf16-rounded weights
+  float lsum_r = 0.0f;  // sum of fp16-rounded weights
   const float c = p.scale_log2;
 
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
@@ -195,6 +207,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const FA_LDS char* kt = kbuf(PAR);
     const FA_LDS char* vt = vbuf(PAR ^ 1);
     const int k0 = j * BN;
+    int e_cur = 0;  // power-of-two exponent of tile j's fp16 V copy (wave-uniform)
+    if constexpr (NEXT) e_cur = v_exp[k0];
 
     // -- phase 1: S(j)'s MFMAs, with the exponentials of tile j-1's first 32-key
     // block (with their sums and bf16 packing) between them.  The second block's
@@ -205,14 +219,14 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four partial sums: short dependency chains
     auto exp_pair = [&](const int q) {  // scores 2u, 2u+1 of block kb = q / 8 of tile j-1
       const int kb = q >> 3, u = q & 7, e = 2 * u;
-      // P = 2^(s*c - m*c) -> bf16 operands; the fp32 weights feed the LSE sum
-      const float x0 = __builtin_fmaf(s_prev[kb][e], c, -mref);
-      const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref);
+      // P' = 2^(s*c - m*c + e) = P 2^e -> fp16 operands; the fp32 weights feed the LSE sum
+      const float x0 = __builtin_fmaf(s_prev[kb][e], c, -mref_x);
+      const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref_x);
       const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
       const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
       rs[u & 3] += p0;
       rs[u & 3] += p1;
-      pb[2 * kb + (u >> 2)][u & 3] = pack_bf16(p0, p1);
+      pb[2 * kb + (u >> 2)][u & 3] = pack_f16(p0, p1);
     };
     constexpr int NPAIR = 8 * NKB;   // pairs of scores per lane and tile
     constexpr int P1 = 8;            // pairs of phase 1: the first block
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
             exp_pair(q);
           const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
           const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
-          oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
+          oacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
           if constexpr (NEXT) {
             // two scores of S(j) per MFMA, 32 in all
 #pragma unroll
@@ -287,13 +301,13 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
           }
         }
       }
-      // sum of the bf16-rounded weights the products used: O is normalised by it, so
+      // sum of the fp16-rounded weights the products used: O is normalised by it, so
       // a dominant weight's rounding cancels between numerator and denominator (with a
       // stale reference that weight is up to 2^8, not 1)
 #pragma unroll
       for (int g = 0; g < BN / 16; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rsr[e & 1] = add_bf16_pair(pb[g][e], rsr[e & 1]);
+        for (int e = 0; e < 4; ++e) rsr[e & 1] = add_f16_pair(pb[g][e], rsr[e & 1]);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
       for (int i = 0; i < NM2 / 2; ++i) {
@@ -309,8 +323,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       }
       // the empty asm makes the sums exist here, so their adds are scheduled among
       // this phase's MFMAs instead of being sunk past the rescale branch
-      lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-      lsum_r += rsr[0] + rsr[1];
+      lsum += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * esc;
+      lsum_r += (rsr[0] + rsr[1]) * esc;
       asm volatile("" : "+v"(lsum), "+v"(lsum_r));
       __builtin_amdgcn_sched_barrier(0);
     } else if constexpr (NEXT) {
@@ -324,10 +338,15 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       // row maximum across the two wave halves; lazy rescale: move the reference
       // only when the maximum grew by more than TAU.  O and the sums then hold
       // everything up to tile j-1 and are scaled before tile j's weights are added.
+      // A tile whose V copy needed e > 7 (|V| >= 2^15) moves every reference that
+      // grew, so that its weights stay <= 1 and P 2^e <= 2^15 fits fp16.
       mx = half_swap_max(mx);
       const float m_new = fmaxf(m_used, mx);
       bool need = m_new > m_used;
-      if constexpr (TAU > 0) need = need && (m_used == -INFINITY || (m_new - m_used) * c > (float)TAU);
+      if constexpr (TAU > 0) {
+        const float tau = e_cur > 7 ? 0.0f : (float)TAU;
+        need = need && (m_used == -INFINITY || (m_new - m_used) * c > tau);
+      }
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float alpha = need ? (m_used == -INFINITY ? 0.0f : exp2_hw((m_used - m_new) * c)) : 1.0f;
         m_used = need ? m_new : m_used;
@@ -339,6 +358,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
+      mref_x = mref - (float)e_cur;
+      esc = __int_as_float((127 - e_cur) << 23);
     }
   };
 
@@ -385,7 +406,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     if (j < n_tiles) issue(rv, v_ss2, j, vbuf(par));
   }
 
-  // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l ----
+  // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l (O_acc and the sums are in
+  // true units: each tile's 2^e on the weights cancels the 2^-e on its V copy) ----
   const float lt = half_swap_sum(lsum);
   const float ltr = half_swap_sum(lsum_r);
   const float inv = ltr > 0.0f ? 1.0f / ltr : 0.0f;
@@ -417,6 +439,88 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       }
     if (hl == 0 && my_row < Lq) p.lse[lseoff + my_row] = lse;
   }
+}
+
+// ---- fp16 copy of V with one power-of-two scale per 64-key tile ----
+// One workgroup per (tile, sequence, head).  The weights P' = P 2^e go to fp16 with
+// P <= 2^8 (the lazy bound), so e <= 7 keeps them finite; the largest e keeps the most
+// weights in fp16's normal range (a row's many small weights carry much of its mass,
+// and a subnormal weight has few bits).  So e = 7, and the copy is V 2^-7: a bf16
+// value (8 significant bits) then converts exactly unless it falls below 2^-7 in
+// magnitude, where the fp16 subnormal it becomes is off by less than 2^-18.  With
+// E the exponent of the tile's largest |v| (a bf16 value widens exactly):
+//   E < -4:       e = max(E + 11, -10), so that a tile of tiny values keeps its
+//                 largest elements normal in the copy;
+//   -4 <= E <= 22: e = 7 (the copy stays below 2^16);
+//   E > 22:       e = E - 15 (at most 15); the forward then moves every growing row
+//                 reference on that tile, so that its weights stay <= 1 and P 2^e fits;
+//                 |v| must stay below 2^31.
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(256) void vprep_kernel(FwdParams p) {
+  constexpr int BN = kFwdBlockN;
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int PER = BN * CPR / 256;      // chunks per thread
+  __shared__ uint32_t wmax[4];
+  const int t = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+  int Lk = p.seqlen_k;
+  int64_t voff, krow0;
+  if constexpr (VARLEN) {
+    const int sk = p.cu_k[b];
+    Lk = p.cu_k[b + 1] - sk;
+    voff = (int64_t)sk * p.v_ss + (int64_t)h * p.v_sh;
+    krow0 = sk;
+  } else {
+    voff = (int64_t)b * p.v_sb + (int64_t)h * p.v_sh;
+    krow0 = (int64_t)b * Lk;
+  }
+  const int r_first = t * BN;
+  if (r_first >= Lk) return;
+  const uint16_t* src = (const uint16_t*)p.v + voff;
+  u32x4 v[PER];
+  uint32_t mx = 0;  // largest |v| as a bf16 magnitude pattern (ordered like the values)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = i * 256 + threadIdx.x;
+    const int r = r_first + idx / CPR, cc = idx % CPR;
+    v[i] = r < Lk ? *(const u32x4*)(src + (int64_t)r * p.v_ss + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = max(mx, max(v[i][w] & 0x7FFFu, (v[i][w] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int E = (int)(mx >> 7) - 127;  // -127 for an all-zero tile
+  const int e = E > 22 ? min(E - 15, 15) : min(max(E + 11, -10), 7);
+  const float sc = __int_as_float((127 - e) << 23);  // 2^-e, exact
+  uint16_t* dst = p.v16 + ((int64_t)h * p.total_k + krow0) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = i * 256 + threadIdx.x;
+    const int r = r_first + idx / CPR, cc = idx % CPR;
+    if (r < Lk) {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = pack_f16(bf16_lo(v[i][w]) * sc, bf16_hi(v[i][w]) * sc);
+      *(u32x4*)(dst + (int64_t)r * D + cc * 8) = o;
+    }
+  }
+  if (threadIdx.x == 0) p.v_exp[(int64_t)h * p.total_k + krow0 + r_first] = e;
+}
+
+hipError_t launch_fwd_vprep(const FwdParams& p, int head_dim, bool varlen, hipStream_t stream) {
+  const int tiles = (p.seqlen_k + kFwdBlockN - 1) / kFwdBlockN;  // seqlen_k: the longest key sequence
+  if (tiles == 0 || p.batch == 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles, (unsigned)p.batch, (unsigned)p.heads);
+  if (head_dim == 128) {
+    if (varlen) hipLaunchKernelGGL((vprep_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((vprep_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (varlen) hipLaunchKernelGGL((vprep_kernel<64, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((vprep_kernel<64, false>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 // ---- merge of the key chunks' partial results ----

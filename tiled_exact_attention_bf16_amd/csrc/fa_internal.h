@@ -39,6 +39,12 @@ struct FwdParams {
   int n_split;
   float* part_lse;
   float* part_o;
+  // fp16 copy of V for the PV product, [H, total_k, D] over the packed or batched key
+  // rows (b*seqlen_k + j for fixed length), each 64-key tile of a sequence scaled by
+  // 2^-e with e = v_exp[h*total_k + first row of the tile] (see vprep_kernel)
+  int total_k;
+  uint16_t* v16;
+  int32_t* v_exp;
 };
 
 struct FwdConfig {
@@ -53,6 +59,9 @@ struct FwdConfig {
 
 // Returns hipSuccess or the launch error.  Grid size is derived from p and cfg.
 hipError_t launch_fwd(const FwdParams& p, const FwdConfig& cfg, hipStream_t stream);
+
+// Writes the fp16 copy of V and the per-tile exponents into p.v16 / p.v_exp.
+hipError_t launch_fwd_vprep(const FwdParams& p, int head_dim, bool varlen, hipStream_t stream);
 
 // Builds the longest-first list {count, (seq, tile)...} for variable length.
 hipError_t launch_fwd_schedule(const int32_t* cu_q, const int32_t* cu_k, int batch, int tile_rows,
