@@ -256,6 +256,24 @@ enum { FA_BWD_PHASE_PRE = 1, FA_BWD_PHASE_MAIN = 2, FA_BWD_PHASE_POST = 4, FA_BW
 fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* The backward of fa_bwd (same arguments, results and errors) for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Its workspace is a static device
+ * array inside the library (fa_bwd_noalloc_scratch_bytes() bytes, 64 MiB, one copy
+ * per GPU, held until the process ends); the call allocates nothing.  A request whose
+ * workspace (fa_bwd_workspace_size) exceeds that size returns
+ * FA_ERR_WORKSPACE_TOO_SMALL before any device work: the deterministic mode needs
+ * 4 bytes per query row and head (plus the work lists of variable-length batches),
+ * the atomic mode 4 * (head_dim + 1) bytes per query row and head.  Every call on a
+ * GPU uses that GPU's one array, whose contents carry over from the last call (each
+ * call writes everything it reads): calls that overlap in time on one GPU -- on
+ * different streams, or from different threads -- race and give undefined
+ * gradients.  FA_ERR_HIP if the array's address cannot be obtained. */
+fa_status fa_bwd_noalloc(const fa_bwd_args* a, void* stream);
+
+/* Size in bytes of the static workspace fa_bwd_noalloc uses. */
+size_t fa_bwd_noalloc_scratch_bytes(void);
+
 /* Static name of a status code, e.g. "FA_ERR_UNSUPPORTED" ("FA_ERR_UNKNOWN" for a
  * value outside the enum; never NULL).  The codes are this library's own; the
  * pages define no interface (the argument set follows the operation: Q, K, V, the

@@ -263,3 +263,20 @@ def test_exp2_probe_validation():
     assert lib.fa_exp2_probe(None, None, None, -1, None) == L.FA_ERR_INVALID_ARGUMENT
     assert lib.fa_exp2_probe(None, None, None, 5, None) == L.FA_ERR_INVALID_ARGUMENT
     assert lib.fa_exp2_probe(None, None, None, 0, None) == L.FA_OK  # nothing to do, no device call
+
+
+def test_noalloc_backward_rejects_before_touching_the_gpu():
+    lib = L.lib()
+    assert lib.fa_bwd_noalloc_scratch_bytes() == 64 << 20
+    assert lib.fa_bwd_noalloc(None, None) == L.FA_ERR_INVALID_ARGUMENT
+    bad = bwd_args()
+    bad.head_dim = 96
+    assert lib.fa_bwd_noalloc(ctypes.byref(bad), None) == L.FA_ERR_UNSUPPORTED
+    # atomic mode: 4 * (128 + 1) bytes per query row and head; 16 heads x 32768 rows exceed 64 MiB
+    big = bwd_args(b=4, s=8192, h=16, det=0)
+    st, need = bwd_ws(big)
+    assert st == L.FA_OK and need > 64 << 20
+    assert lib.fa_bwd_noalloc(ctypes.byref(big), None) == L.FA_ERR_WORKSPACE_TOO_SMALL
+    # the same shape in deterministic mode fits (4 bytes per row and head)
+    fits = bwd_args(b=4, s=8192, h=16, det=1)
+    assert bwd_ws(fits)[1] <= 64 << 20

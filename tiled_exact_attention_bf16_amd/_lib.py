@@ -80,6 +80,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (c_int32, [POINTER(BwdArgs), POINTER(c_size_t)]),
     "fa_bwd": (c_int32, [POINTER(BwdArgs), c_void_p, c_size_t, c_void_p]),
     "fa_bwd_phases": (c_int32, [POINTER(BwdArgs), c_int32, c_void_p, c_size_t, c_void_p]),
+    "fa_bwd_noalloc": (c_int32, [POINTER(BwdArgs), c_void_p]),
+    "fa_bwd_noalloc_scratch_bytes": (c_size_t, []),
     "fa_status_str": (c_char_p, [c_int32]),
     "fa_version": (c_char_p, []),
 }

@@ -258,6 +258,33 @@ def bwd_args(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale, causal, determini
     return a
 
 
+def bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                softmax_scale: Optional[float] = None, causal: bool = False, deterministic: bool = False,
+                cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+                max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None, stream=None):
+    """The backward through fa_bwd_noalloc: the library's static workspace, no device
+    allocation anywhere in the call (the caller passes dq, dk, dv; their dtype is the
+    gradient dtype)."""
+    grad_dtype = dq.dtype
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dq must be float32 or bfloat16")
+    _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_tensor("o", o, torch.bfloat16, q.shape)
+    _check_tensor("dout", dout, torch.bfloat16, q.shape)
+    _check_lse(lse, q, cu_seqlens_q is not None)
+    for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, g, grad_dtype, ref.shape)
+    _check_devices(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, cu_seqlens_q=cu_seqlens_q,
+                   cu_seqlens_k=cu_seqlens_k)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    a = bwd_args(dout, q, k, v, o, lse, dq, dk, dv, softmax_scale, causal, deterministic, grad_dtype,
+                 cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    L.check(L.lib().fa_bwd_noalloc(ctypes.byref(a), _stream(stream)), "fa_bwd_noalloc")
+    return dq, dk, dv
+
+
 def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         lse: torch.Tensor, softmax_scale: Optional[float] = None, causal: bool = False,
         deterministic: bool = False, grad_dtype: torch.dtype = torch.float32,

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_gfx950.h"
 #include "fa_internal.h"
@@ -344,6 +345,30 @@ BwdLayout bwd_layout(const Shape& s, bool deterministic) {
   return l;
 }
 
+// Scratch of the allocation-free backward (fa_bwd_noalloc): a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol): each
+// device's address is looked up once, with that device current, and kept here.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch`, or nullptr on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes) {
@@ -358,6 +383,19 @@ fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes) {
 fa_status fa_bwd(const fa_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_bwd_phases(a, FA_BWD_PHASE_ALL, workspace, workspace_bytes, stream);
 }
+
+fa_status fa_bwd_noalloc(const fa_bwd_args* a, void* stream) {
+  // every argument, and the workspace the request needs, is checked before any HIP call
+  Shape s;
+  fa_status st = check_bwd(a, &s);
+  if (st != FA_OK) return st;
+  if (bwd_layout(s, a->deterministic != 0).total > kNoallocScratchBytes) return FA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = device_scratch();
+  if (ws == nullptr) return FA_ERR_HIP;
+  return fa_bwd_phases(a, FA_BWD_PHASE_ALL, ws, kNoallocScratchBytes, stream);
+}
+
+size_t fa_bwd_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, size_t workspace_bytes,
                         void* stream) {
