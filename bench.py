@@ -23,7 +23,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA, AMD's published 2.5 PFLOP/s (256 CU x 2.4 GHz x 4096
+                            # FLOP/clk/CU = 2516.6 before rounding)
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "headline"       # causal B=2 H=16 S=8192 d=128
 COPY_BYTES = 1 << 30        # calibration copy: 1 GiB read + 1 GiB written
@@ -61,6 +62,64 @@ def recorded_traffic(phase: str):
     return None
 
 
+class ClockSampler:
+    """Shader clock during the timed region: the current level of the driver's DPM table
+    (/sys/class/drm/card*/device/pp_dpm_sclk, the line marked '*'), read every 2 ms by a
+    background thread (a file read; nothing touches the GPU)."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:1]
+        self.mhz = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for f in self.files:
+            try:
+                for ln in open(f).read().splitlines():
+                    if ln.rstrip().endswith("*"):
+                        return float(ln.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+            except (OSError, ValueError, IndexError):
+                return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.mhz.append(v)
+            time.sleep(0.002)
+
+    def __enter__(self):
+        if self.files:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.files:
+            self._t.join()
+
+    def summary(self):
+        busy = [m for m in self.mhz if m >= 500]  # drop deep-sleep readings between kernels
+        if not busy:
+            return None
+        return {"mean_mhz": round(float(np.mean(busy)), 1), "min_mhz": min(busy), "max_mhz": max(busy),
+                "samples": len(busy), "source": "pp_dpm_sclk current level, sampled every 2 ms"}
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, budget_s: float = 12.0, max_heads: int = 8):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload:
     forward then backward of whole (sequence, head) pairs, until ``budget_s``."""
@@ -86,6 +145,7 @@ def cpu_baseline(inp, budget_s: float = 12.0, max_heads: int = 8):
         if t_total >= budget_s:
             break
     return {"value": round(flop / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 numpy forward+backward of {done} whole (sequence, head) pairs of the "
                       f"{inp.q.shape[1]}-token causal workload, {t_total:.1f} s"}
 
@@ -116,12 +176,16 @@ def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
         ws_f = FA.fwd_workspace(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx)
         o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx, workspace=ws_f)
         dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in (q, k, v))
-        ws_b = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")  # atomic c4: 1.07 GB accumulator
         run = {"fwd": lambda: FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx,
                                      out=o, lse=lse, workspace=ws_f),
                "bwd": lambda: FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, cu_seqlens_q=cu,
                                      max_seqlen_q=mx, deterministic=deterministic, dq=dq, dk=dk, dv=dv,
-                                     workspace=ws_b)}
+                                     workspace=ws_b),
+               "bwd_" + ("atomic" if deterministic else "deterministic"):
+                   lambda: FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, cu_seqlens_q=cu,
+                                  max_seqlen_q=mx, deterministic=not deterministic, dq=dq, dk=dk, dv=dv,
+                                  workspace=ws_b)}
         row = {}
         # the 4096-token workloads (K+V 128 MiB) fit in the 256 MB last-level cache: time
         # them also with a 512 MiB scratch write between calls (outside the timed region)
@@ -150,6 +214,50 @@ def time_all_configs(deterministic: bool, warmup: int = 10, iters: int = 50):
         del q, k, v, do, o, lse, dq, dk, dv, ws_f, ws_b
         torch.cuda.empty_cache()
     return res
+
+
+def run_workload(name: str, steps: int, warmup: int, deterministic: bool, tau: int = -1):
+    """Forward then backward of one named workload, `steps` times after `warmup` (for
+    profiling one workload under rocprofv3); prints per-phase HIP-event averages."""
+    import torch
+    from tiled_exact_attention_bf16_amd import _lib as L
+    from tiled_exact_attention_bf16_amd import attention as FA
+    from tiled_exact_attention_bf16_amd import inputs as I
+    from tiled_exact_attention_bf16_amd import workload as W
+    inp = I.make_inputs(name)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    do = dev(inp.do) if inp.do is not None else torch.randn(q.shape, device="cuda").to(torch.bfloat16)
+    cu = torch.from_numpy(inp.cu_seqlens).cuda() if inp.varlen else None
+    mx = inp.max_seqlen() if inp.varlen else None
+    t = FA.Tuning(rescale_threshold_log2=tau)
+    ws_f = FA.fwd_workspace(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx, tuning=t)
+    ws_b = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    o, lse = FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx, workspace=ws_f, tuning=t)
+    dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v))
+    fns = {"fwd": lambda: FA.fwd(q, k, v, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx, out=o, lse=lse,
+                                 workspace=ws_f, tuning=t),
+           "bwd": lambda: FA.bwd(do, q, k, v, o, lse, inp.scale, inp.causal, cu_seqlens_q=cu, max_seqlen_q=mx,
+                                 deterministic=deterministic, dq=dq, dk=dk, dv=dv, workspace=ws_b)}
+    for _ in range(warmup):
+        for fn in fns.values():
+            fn()
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for n in fns}
+    for i in range(steps):
+        for n, fn in fns.items():
+            ev[n][i][0].record()
+            fn()
+            ev[n][i][1].record()
+    torch.cuda.synchronize()
+    lens = [int(x) for x in inp.seqlens()]
+    fl = {"fwd": W.fwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal),
+          "bwd": W.bwd_flops(lens, lens, inp.num_heads, q.shape[-1], inp.causal)}
+    res = {}
+    for n in fns:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
+        res[n] = {"ms": round(ms, 4), "tflops": round(fl[n] / (ms * 1e-3) / 1e12, 2)}
+    print(json.dumps({"workload": name, "deterministic": deterministic, "tau": tau, **res}), flush=True)
 
 
 def time_decode(warmup: int = 10, iters: int = 50):
@@ -204,6 +312,9 @@ def main():
     ap.add_argument("--tau", type=int, default=-1)
     ap.add_argument("--all-configs", action="store_true",
                     help="also time forward and backward of every named workload (median/min of 50)")
+    ap.add_argument("--workload", default=None,
+                    help="only run forward+backward of this named workload (c1..c5, c2_causal, headline) "
+                         "--steps times and print per-phase averages (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain device copy of a known size (for scaling HBM counters)")
     args = ap.parse_args()
@@ -222,6 +333,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     L.lib()  # fail loudly if the HIP library is missing
+    if args.workload:
+        run_workload(args.workload, args.steps, args.warmup, not args.atomic, args.tau)
+        return
 
     inp = I.make_inputs(BWD_SEED_CONFIG)   # B=2 S=8192 H=16 d=128 causal, with dO
     B, S, H, D = inp.q.shape
@@ -254,20 +368,21 @@ def main():
     names = ["fwd", "bwd_pre", "bwd_main", "bwd_post"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        e[0].record()
-        fwd()
-        e[1].record()
-        bwd(L.FA_BWD_PHASE_PRE)
-        e[2].record()
-        bwd(L.FA_BWD_PHASE_MAIN)
-        e[3].record()
-        bwd(L.FA_BWD_PHASE_POST)
-        e[4].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            e = ev[i]
+            e[0].record()
+            fwd()
+            e[1].record()
+            bwd(L.FA_BWD_PHASE_PRE)
+            e[2].record()
+            bwd(L.FA_BWD_PHASE_MAIN)
+            e[3].record()
+            bwd(L.FA_BWD_PHASE_POST)
+            e[4].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     if args.copy_calibration:
         # outside the timed region: one copy kernel reading and writing COPY_BYTES
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -286,7 +401,9 @@ def main():
     fwd_tf = f_fwd / (per["fwd"] * 1e-3) / 1e12
     bwd_ms = per["bwd_pre"] + per["bwd_main"] + per["bwd_post"]
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
-    value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    # whole-step throughput from the wall clock around the timed steps (the same clock as
+    # ms_per_step); the per-kernel events give the breakdown
+    value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
     # algorithmic FLOP per visible pair for each kernel: forward 4d (S, PV); key-block
     # kernel 8d (S, dP, dV, dK) in deterministic mode, 10d with the atomic dQ product;
     # deterministic dQ kernel 2d (dQ; its S and dP are recomputation)
@@ -321,10 +438,38 @@ def main():
         "bwd_tflops": round(bwd_tf, 2),
         "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(per[n], 4) for n in names},
+        "events_step_ms": round(step_ms, 4),
+        "shader_clock": clk.summary(),
         "roofline": {"bound": "mfma", "kernel": kernel_names[dominant], "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dominant) if det or dominant == "fwd" else None},
     }
+    # the other dQ mode of the same backward, outside the timed step (reported beside it)
+    other = not det
+
+    def bwd_other(phases):
+        FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=other, dq=dq, dk=dk, dv=dv, workspace=ws,
+               phases=phases)
+
+    for _ in range(args.warmup):
+        bwd_other(L.FA_BWD_PHASE_ALL)
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = ev2[i]
+        e[0].record()
+        bwd_other(L.FA_BWD_PHASE_PRE)
+        e[1].record()
+        bwd_other(L.FA_BWD_PHASE_MAIN)
+        e[2].record()
+        bwd_other(L.FA_BWD_PHASE_POST)
+        e[3].record()
+    torch.cuda.synchronize()
+    per2 = {n: float(np.mean([ev2[i][j].elapsed_time(ev2[i][j + 1]) for i in range(args.steps)]))
+            for j, n in enumerate(("bwd_pre", "bwd_main", "bwd_post"))}
+    ms2 = sum(per2.values())
+    out["bwd_" + ("deterministic" if other else "atomic")] = {
+        "ms": round(ms2, 4), "tflops": round(f_bwd / (ms2 * 1e-3) / 1e12, 2),
+        "kernel_ms": {n: round(x, 4) for n, x in per2.items()}}
     if args.all_configs:
         out["configs"] = time_all_configs(det)
         out["decode"] = time_decode()

@@ -1,4 +1,5 @@
-"""Device probe of the forward's two exponentials (fa_exp2_probe) on a dense sweep.
+"""Device probe of the forward's two exponentials (fa_exp2_probe) on every fp32 input of
+[-126, 8] (2.21e9 bit patterns) and a 2^24-point uniform grid.
 
 The software 2^x (split into integer and fraction, cubic on the fraction, integer
 added to the exponent bits; FA4 summary page, "Software exponentials" bullet) and the
@@ -23,23 +24,54 @@ if torch.cuda.is_available():
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")))["software_exp2"]
 
 
-def _bf16_bits(x32: np.ndarray) -> np.ndarray:
-    """Round-to-nearest-even bf16 bit patterns of non-negative float32 values."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.int64)
+def _bf16_bits_t(x32: "torch.Tensor") -> "torch.Tensor":
+    """Round-to-nearest-even bf16 bit patterns of non-negative float32 values (int64)."""
+    u = x32.contiguous().view(torch.int32).to(torch.int64) & 0xFFFFFFFF
     return (u + 0x7FFF + ((u >> 16) & 1)) >> 16
 
 
-def _ulps(a32: np.ndarray, b32: np.ndarray) -> np.ndarray:
-    return np.abs(_bf16_bits(a32) - _bf16_bits(b32))
+def _chunks(name: str, chunk: int = 1 << 27):
+    """Every fp32 bit pattern of the range, in chunks (device tensors), or the grid."""
+    if name == "uniform grid":  # 2^24 points uniform in value over [-126, 8]
+        yield torch.linspace(-126.0, 8.0, 1 << 24, dtype=torch.float64, device="cuda").to(torch.float32)
+        return
+    if name == "negative":      # every pattern of [-126, 0): 0x80000001 .. 0xC2FC0000 (and -0)
+        lo, hi = 0x80000000, int(np.array(-126.0, dtype=np.float32).view(np.uint32))
+    else:                       # every pattern of [0, 8]: 0x00000000 .. 0x41000000
+        lo, hi = 0, int(np.array(8.0, dtype=np.float32).view(np.uint32))
+    for a in range(lo, hi + 1, chunk):
+        b = min(hi + 1, a + chunk)
+        bits = torch.arange(a, b, dtype=torch.int64, device="cuda")
+        bits = torch.where(bits >= 1 << 31, bits - (1 << 32), bits).to(torch.int32)
+        yield bits.view(torch.float32)
 
 
-def _sweep(name: str) -> np.ndarray:
-    if name == "negative":   # every 61st fp32 bit pattern of [-126, 0)
-        start = int(np.array(-126.0, dtype=np.float32).view(np.uint32))
-        return np.arange(start, 0x80000000, -61, dtype=np.int64).astype(np.uint32).view(np.float32)
-    if name == "non-negative":  # every 61st fp32 bit pattern of [0, 8]
-        return np.arange(0, int(np.float32(8.0).view(np.uint32)) + 1, 61, dtype=np.uint32).view(np.float32)
-    return np.linspace(-126.0, 8.0, 1 << 22, dtype=np.float32)  # uniform in value
+@pytest.mark.parametrize("name", ["negative", "non-negative", "uniform grid"])
+def test_exp2_probe_dense_sweep(name):
+    # every fp32 bit pattern of [-126, 8] (2.21e9 inputs over the two ranges) plus a
+    # 2^24-point uniform grid; reference: fp64 exp2 rounded to fp32, then to bf16
+    n = ok_poly = ex_poly = ok_hw = ex_hw = ok_pair = ex_pair = 0
+    worst = 0
+    for x in _chunks(name):
+        y_poly, y_hw = FA.exp2_probe(x)
+        ref = torch.exp2(x.to(torch.float64)).to(torch.float32)
+        bp, bh, br = _bf16_bits_t(y_poly), _bf16_bits_t(y_hw), _bf16_bits_t(ref)
+        assert bool(torch.isfinite(y_poly).all()) and bool((y_poly > 0).all())
+        d_poly, d_hw, d_pair = (bp - br).abs(), (bh - br).abs(), (bp - bh).abs()
+        n += x.numel()
+        ok_poly += int((d_poly <= 1).sum()); ex_poly += int((d_poly == 0).sum())
+        ok_hw += int((d_hw <= 1).sum()); ex_hw += int((d_hw == 0).sum())
+        ok_pair += int((d_pair <= 1).sum()); ex_pair += int((d_pair == 0).sum())
+        worst = max(worst, int(d_poly.max()))
+        del x, y_poly, y_hw, ref, bp, bh, br, d_poly, d_hw, d_pair
+    say(f"[exp2 {name}] {n} inputs | software: <=1 ulp {ok_poly / n:.6f}, exact {ex_poly / n:.6f}, max {worst} | "
+        f"v_exp_f32: <=1 ulp {ok_hw / n:.6f}, exact {ex_hw / n:.6f} | "
+        f"software vs v_exp_f32: <=1 ulp {ok_pair / n:.6f}, exact {ex_pair / n:.6f}")
+    share = GOLDEN["fraction_of_inputs"]
+    assert ok_poly / n >= share and ok_hw / n >= share and ok_pair / n >= share
+    if name != "uniform grid":
+        expected = {"negative": 0xC2FC0000 - 0x80000000 + 1, "non-negative": 0x41000000 + 1}[name]
+        assert n == expected
 
 
 def _probe(xs: np.ndarray):
@@ -47,23 +79,6 @@ def _probe(xs: np.ndarray):
     y_poly, y_hw = FA.exp2_probe(x)
     torch.cuda.synchronize()
     return y_poly.cpu().numpy(), y_hw.cpu().numpy()
-
-
-@pytest.mark.parametrize("name", ["negative", "non-negative", "uniform grid"])
-def test_exp2_probe_dense_sweep(name):
-    xs = _sweep(name)
-    say(f"case exp2 sweep {name}: {len(xs)} inputs")
-    y_poly, y_hw = _probe(xs)
-    ref = np.exp2(xs.astype(np.float64)).astype(np.float32)
-    assert np.all(np.isfinite(y_poly)) and np.all(y_poly > 0)
-    share = GOLDEN["fraction_of_inputs"]
-    d_poly, d_hw, d_pair = _ulps(y_poly, ref), _ulps(y_hw, ref), _ulps(y_poly, y_hw)
-    say(f"[exp2 {name}] software: <=1 ulp {np.mean(d_poly <= 1):.6f}, exact {np.mean(d_poly == 0):.6f}, "
-        f"max {d_poly.max()} | v_exp_f32: <=1 ulp {np.mean(d_hw <= 1):.6f}, exact {np.mean(d_hw == 0):.6f} | "
-        f"software vs v_exp_f32: <=1 ulp {np.mean(d_pair <= 1):.6f}, exact {np.mean(d_pair == 0):.6f}")
-    assert np.mean(d_poly <= GOLDEN["max_bf16_ulp"]) >= share
-    assert np.mean(d_hw <= GOLDEN["max_bf16_ulp"]) >= share
-    assert np.mean(d_pair <= GOLDEN["max_bf16_ulp"]) >= share
 
 
 def test_exp2_probe_special_values():

@@ -33,6 +33,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
+#define FA_CONST __attribute__((address_space(4)))
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
