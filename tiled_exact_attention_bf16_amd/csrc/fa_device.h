@@ -138,6 +138,54 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// In-place exclusive prefix sum of hist[0..NB) taken from the last bin down (bin NB-1
+// receives 0, bin c the sum of bins c+1..NB-1), by a whole 1024-thread workgroup:
+// each thread sums a run of bins, the 64-wide waves scan their runs with shuffles,
+// wave 0 scans the 16 wave totals, and each thread writes its run.  Returns the total.
+template <int NB>
+__device__ int scan_bins_descending(int* hist, int* wsum /* 16 ints of LDS */) {
+  constexpr int PER = (NB + 1023) / 1024;
+  const int t = threadIdx.x;
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = t * PER + i;
+    if (d < NB) local += hist[NB - 1 - d];
+  }
+  int x = local;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if ((t & 63) >= o) x += y;
+  }
+  if ((t & 63) == 63) wsum[t >> 6] = x;
+  __syncthreads();
+  if (t < 64) {
+    int w = t < 16 ? wsum[t] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(w, o, 64);
+      if (t >= o) w += y;
+    }
+    if (t < 16) wsum[t] = w;
+  }
+  __syncthreads();
+  int run = x - local + ((t >> 6) > 0 ? wsum[(t >> 6) - 1] : 0);
+  const int total = wsum[15];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = t * PER + i;
+    if (d < NB) {
+      const int c = NB - 1 - d;
+      const int n = hist[c];
+      hist[c] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 // XOR swizzle of the 16-byte slots of a K/V row held in LDS.  Chosen so that (a)
 // 16 consecutive rows read at one column hit 16 different slots (row-major MFMA
 // operand reads) and (b) 4-row groups read through the transpose unit hit

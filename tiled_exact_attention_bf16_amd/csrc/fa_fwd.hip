@@ -573,6 +573,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
 __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const int32_t* cu_k, int batch,
                                                      int tile_rows, int block_n, int causal, int32_t* out) {
   __shared__ int hist[kSchedMaxCost + 1];
+  __shared__ int wsum[16];
   __shared__ int total;
   for (int i = threadIdx.x; i <= kSchedMaxCost; i += blockDim.x) hist[i] = 0;
   if (threadIdx.x == 0) total = 0;
@@ -591,16 +592,8 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const 
     atomicAdd(&total, nt);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int c = kSchedMaxCost; c >= 0; --c) {
-      const int n = hist[c];
-      hist[c] = run;
-      run += n;
-    }
-    out[0] = total;
-  }
-  __syncthreads();
+  scan_bins_descending<kSchedMaxCost + 1>(hist, wsum);
+  if (threadIdx.x == 0) out[0] = total;
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
     const int lq = cu_q[b + 1] - cu_q[b];
     const int nt = (lq + tile_rows - 1) / tile_rows;
