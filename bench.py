@@ -108,7 +108,8 @@ class ClockSampler:
             return None
         return {"mean_mhz": round(float(np.mean(self.mhz)), 1), "min_mhz": round(min(self.mhz), 1),
                 "max_mhz": round(max(self.mhz), 1), "samples": len(self.mhz),
-                "source": "amdsmi current_gfxclks (mean over XCDs), every 5 ms from warm-up to the last timed step"}
+                "source": "amdsmi current_gfxclks (mean over XCDs), every 5 ms from warm-up through 0.3 s "
+                          "of the same step after the timed region"}
 
 
 def cpu_model() -> str:
@@ -384,6 +385,13 @@ def main():
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the driver's clock readings refresh about every 100 ms: keep sampling through
+    # 0.3 s more of the same step, outside the timed region
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < 0.3:
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
     clk.__exit__(None, None, None)
     if args.copy_calibration:
         # outside the timed region: one copy kernel reading and writing COPY_BYTES

@@ -197,9 +197,10 @@ def test_backward_workspace_sizes():
     st, n_atomic = bwd_ws(bwd_args(det=0))
     assert st == L.FA_OK
     rows = 2 * 256 * 4
-    assert n_atomic >= rows * 128 * 4 + rows * 4          # fp32 dQ accumulator + row terms
+    copies = 2 * rows * 128 * 2                           # fp16 copies of Q and K
+    assert n_atomic >= rows * 128 * 4 + rows * 4 + copies  # fp32 dQ accumulator + row terms + copies
     st, n_det = bwd_ws(bwd_args(det=1))
-    assert st == L.FA_OK and rows * 4 <= n_det < n_atomic  # no accumulator in deterministic mode
+    assert st == L.FA_OK and rows * 4 + copies <= n_det < n_atomic  # no accumulator in deterministic mode
 
 
 def test_key_split_workspace_and_validation():
@@ -272,11 +273,15 @@ def test_noalloc_backward_rejects_before_touching_the_gpu():
     bad = bwd_args()
     bad.head_dim = 96
     assert lib.fa_bwd_noalloc(ctypes.byref(bad), None) == L.FA_ERR_UNSUPPORTED
-    # atomic mode: 4 * (128 + 1) bytes per query row and head; 16 heads x 32768 rows exceed 64 MiB
-    big = bwd_args(b=4, s=8192, h=16, det=0)
+    # deterministic mode: 4 + 2 * head_dim bytes per query row and head, 2 * head_dim per
+    # key row and head (row terms and the fp16 copies of Q and K): B=1, S=4096, H=16
+    # fits in 64 MiB, B=2, S=8192 does not
+    fits = bwd_args(b=1, s=4096, h=16, det=1)
+    assert bwd_ws(fits)[1] <= 64 << 20
+    big = bwd_args(b=2, s=8192, h=16, det=1)
     st, need = bwd_ws(big)
     assert st == L.FA_OK and need > 64 << 20
     assert lib.fa_bwd_noalloc(ctypes.byref(big), None) == L.FA_ERR_WORKSPACE_TOO_SMALL
-    # the same shape in deterministic mode fits (4 bytes per row and head)
-    fits = bwd_args(b=4, s=8192, h=16, det=1)
-    assert bwd_ws(fits)[1] <= 64 << 20
+    atomic = bwd_args(b=1, s=8192, h=16, det=0)         # + 4 * head_dim per query row and head
+    assert bwd_ws(atomic)[1] > 64 << 20
+    assert lib.fa_bwd_noalloc(ctypes.byref(atomic), None) == L.FA_ERR_WORKSPACE_TOO_SMALL

@@ -324,8 +324,10 @@ fa_status check_bwd(const fa_bwd_args* a, Shape* s) {
   return FA_OK;
 }
 
+// Backward workspace: [fp32 dQ accumulator (atomic mode)] [row terms D_i] [work lists
+// (variable length)] [maxima for the fp16 exponents] [Q16: H x total_q x D] [K16]
 struct BwdLayout {
-  size_t dq_acc, dvec, sched, total;
+  size_t dq_acc, dvec, sched, stats, q16, k16, total;
 };
 
 BwdLayout bwd_layout(const Shape& s, bool deterministic) {
@@ -341,6 +343,12 @@ BwdLayout bwd_layout(const Shape& s, bool deterministic) {
     const size_t q_items = (size_t)(s.total_q + fa::kFwdTileRows - 1) / fa::kFwdTileRows + s.batch;
     off += round_up(sizeof(int32_t) * (1 + 2 * kv_items + 1 + 2 * q_items));
   }
+  l.stats = off;
+  off += round_up(4 * sizeof(uint32_t) * (1 + (size_t)fa::kBwdPreBlocks));
+  l.q16 = off;
+  off += round_up(sizeof(uint16_t) * (size_t)s.total_q * s.heads * s.d);
+  l.k16 = off;
+  off += round_up(sizeof(uint16_t) * (size_t)s.total_k * s.heads * s.d);
   l.total = off;
   return l;
 }
@@ -441,6 +449,9 @@ fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, s
   p.dq_acc = a->deterministic ? nullptr : (float*)(ws + lay.dq_acc);
   p.dvec = (float*)(ws + lay.dvec);
   p.sched = s.varlen ? (int32_t*)(ws + lay.sched) : nullptr;
+  p.stats = (uint32_t*)(ws + lay.stats);
+  p.q16 = (uint16_t*)(ws + lay.q16);
+  p.k16 = (uint16_t*)(ws + lay.k16);
   return fa::launch_bwd(p, phases, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

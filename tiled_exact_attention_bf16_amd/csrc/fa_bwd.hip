@@ -10,7 +10,8 @@
 //   dK = scale * dS^T Q,   dQ = scale * dS K
 //
 // Kernels (all on the caller's stream):
-//   bwd_pre:  D_i for every row and head; zeroes the fp32 dQ accumulator.
+//   bwd_pre:  D_i for every row and head; the maxima behind the fp16 exponents;
+//             zeroes the fp32 dQ accumulator.  bwd_convert then writes Q16 and K16.
 //   bwd_kv:   one workgroup per block of 128 keys (4 waves x 32 keys) keeps dK and
 //             dV in registers and walks the query tiles of 64 rows that can see
 //             its keys.  Atomic mode: dS goes through LDS (transposed by the
@@ -21,9 +22,14 @@
 //             is reduced in a fixed order with no atomics.
 //   bwd_post: atomic mode: copies the scaled fp32 accumulator into dQ's layout and
 //             dtype.
-// dS is split into a bf16 high part and a bf16 low part (dS - hi) before the dQ
-// and dK products, so those products see dS to about 16 significant bits while
-// every matrix-core operation stays BF16.
+// dS enters the dQ and dK products in fp16 (11 significant bits; bf16's 8 would leave
+// up to ~8e-3 of error on config 5's gradients), so Q and K enter those products --
+// and, to share one copy, S = Q K^T -- as exact fp16 copies made by the pre phase.
+// Three power-of-two exponents keep every fp16 operand in range: Q16 = Q 2^-a and
+// K16 = K 2^-b from the largest |q| and |k|, dS16 = dS 2^-f from the bound
+// |dS_ij| <= scale |dO_i . (v_j - O_i)| <= 2 scale max_i ||dO_i|| max_j ||v_j||;
+// S picks up 2^(a+b) in the exponent's multiplier and dK, dQ are scaled back by
+// 2^(f+a), 2^(f+b) when written.  dP = dO V^T and dV = P^T dO stay BF16.
 #include <algorithm>
 
 #include <type_traits>
@@ -40,7 +46,8 @@ struct BwdSeq {
   int Lq, Lk;
   int64_t qoff, koff, voff, ooff, dooff, dqoff, dkoff, dvoff;  // element offsets
   int64_t lseoff;   // offset of row 0 in the LSE array
-  int64_t rowbase;  // row index of row 0 in the [H, total_q] row-term arrays
+  int64_t rowbase;  // row index of row 0 in the [H, total_q] row-term arrays (and Q16)
+  int64_t krowbase; // row index of key 0 in the [H, total_k] rows of K16
 };
 
 __device__ __forceinline__ BwdSeq bwd_seq(const BwdParams& p, int b, int h) {
@@ -59,6 +66,7 @@ __device__ __forceinline__ BwdSeq bwd_seq(const BwdParams& p, int b, int h) {
     s.dvoff = sk * p.dv_ss + h * p.dv_sh;
     s.lseoff = (int64_t)h * p.total_q + sq;
     s.rowbase = (int64_t)h * p.total_q + sq;
+    s.krowbase = (int64_t)h * p.total_k + sk;
   } else {
     s.Lq = p.seqlen_q;
     s.Lk = p.seqlen_k;
@@ -72,8 +80,81 @@ __device__ __forceinline__ BwdSeq bwd_seq(const BwdParams& p, int b, int h) {
     s.dvoff = b * p.dv_sb + h * p.dv_sh;
     s.lseoff = ((int64_t)b * p.heads + h) * p.seqlen_q;
     s.rowbase = (int64_t)h * p.total_q + (int64_t)b * p.seqlen_q;
+    s.krowbase = (int64_t)h * p.total_k + (int64_t)b * p.seqlen_k;
   }
   return s;
+}
+
+// floor(log2 x) of a non-negative float given by its bits; -127 for 0
+__device__ __forceinline__ int exp_of(uint32_t bits) { return (int)((bits >> 23) & 0xFFu) - 127; }
+
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((127 + e) << 23); }  // |e| <= 126
+
+// The fp16 exponents from the pre pass's maxima: the largest |q| (|k|) lands in
+// [2^14, 2^15) of Q16 (K16), and the dS bound below 2^15, so nothing can overflow
+// fp16 (largest 65504) and only values 2^28 below the largest become subnormal.
+__device__ __forceinline__ BwdExp bwd_exponents(const BwdParams& p) {
+  const FA_CONST uint32_t* st = (const FA_CONST uint32_t*)p.stats;
+  BwdExp e;
+  e.a = min(max(exp_of(st[0]) - 14, -100), 100);
+  e.b = min(max(exp_of(st[1]) - 14, -100), 100);
+  const float bound = 2.0f * p.scale * __builtin_sqrtf(__uint_as_float(st[2])) * __builtin_sqrtf(__uint_as_float(st[3]));
+  e.f = min(max(exp_of(__float_as_uint(bound)) - 14, -100), 100);
+  e.a = __builtin_amdgcn_readfirstlane(e.a);
+  e.b = __builtin_amdgcn_readfirstlane(e.b);
+  e.f = __builtin_amdgcn_readfirstlane(e.f);
+  return e;
+}
+
+// stats[4 + 4g + i] holds block g's maximum of quantity i; one workgroup reduces them
+// into stats[0..3] (every block of the pre pass writes its four slots, so nothing
+// needs clearing between calls)
+__global__ __launch_bounds__(1024) void bwd_reduce_stats_kernel(uint32_t* stats, int blocks) {
+  __shared__ uint32_t red[16][4];
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+  for (int g = threadIdx.x; g < blocks; g += 1024)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = max(m[i], stats[4 + 4 * g + i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][i] = m[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    uint32_t r = 0;
+    for (int w = 0; w < 16; ++w) r = max(r, red[w][threadIdx.x]);
+    stats[threadIdx.x] = r;
+  }
+}
+
+// Largest bf16 magnitude among 8 values, as float bits (ordered like the values).
+__device__ __forceinline__ uint32_t max_mag8(u32x4 v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m = max(m, max(v[w] & 0x7FFFu, (v[w] >> 16) & 0x7FFFu));
+  return m << 16;
+}
+
+__device__ __forceinline__ float sumsq8(u32x4 v) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    acc = __builtin_fmaf(bf16_lo(v[w]), bf16_lo(v[w]), acc);
+    acc = __builtin_fmaf(bf16_hi(v[w]), bf16_hi(v[w]), acc);
+  }
+  return acc;
+}
+
+// Block-wide maximum of one value per thread (256 threads), written by thread 0.
+__device__ __forceinline__ void block_max_store(uint32_t v, uint32_t* dst, uint32_t* lds4) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) *dst = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+  __syncthreads();
 }
 
 __device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t stride_elems, int row_bytes) {
@@ -81,40 +162,81 @@ __device__ __forceinline__ uint32_t rows_bytes(int rows, int64_t stride_elems, i
 }
 
 // ---------------------------------------------------------------------------
-// bwd_pre: D_i = sum_d dO_id O_id (fp32) and zeroing of the dQ accumulator.
-// 16-byte chunks: D/8 lanes per (row, head), reduced with xor shuffles.
+// bwd_pre: D_i = sum_d dO_id O_id (fp32), each block's maxima behind the fp16
+// exponents (|q|, |k|, ||dO_i||^2, ||v_j||^2, reduced afterwards by bwd_reduce_stats)
+// and zeroing of the dQ accumulator.  16-byte chunks: D/8 lanes per (row, head), reduced
+// with xor shuffles.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc) {
   constexpr int CPR = D / 8;  // chunks per row
+  __shared__ uint32_t red[4];
   const int64_t total_rows = (int64_t)p.total_q * p.heads;
+  const int64_t total_krows = (int64_t)p.total_k * p.heads;
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t w = tid; w < total_rows * CPR; w += nthreads) {
+  // element offset of (row, head) in a [B,S,H,D] / [T,H,D] tensor; row counts the
+  // packed or batched rows (b * seqlen + s for fixed length)
+  auto offs = [&](int64_t row, int h, int64_t sb, int64_t ss, int64_t sh, int seqlen) {
+    if (p.varlen) return row * ss + h * sh;
+    const int64_t b = row / seqlen, t = row - b * seqlen;
+    return b * sb + t * ss + h * sh;
+  };
+  float do2 = 0.0f;
+  uint32_t qmax = 0;
+  // loops sized to a whole number of rows per pass, so the xor reductions see full rows
+  for (int64_t w = tid; w < ((total_rows * CPR + 63) / 64) * 64; w += nthreads) {
     const int64_t rh = w / CPR;
     const int chunk = (int)(w - rh * CPR);
-    const int h = (int)(rh / p.total_q);
-    const int64_t row = rh - (int64_t)h * p.total_q;  // global packed row (b*S + s for fixed)
-    int64_t obase, dobase;
-    if (p.varlen) {
-      obase = row * p.o_ss + h * p.o_sh;
-      dobase = row * p.do_ss + h * p.do_sh;
-    } else {
-      const int64_t b = row / p.seqlen_q, s = row - b * p.seqlen_q;
-      obase = b * p.o_sb + s * p.o_ss + h * p.o_sh;
-      dobase = b * p.do_sb + s * p.do_ss + h * p.do_sh;
-    }
-    const u32x4 ov = *(const u32x4*)((const uint16_t*)p.o + obase + chunk * 8);
-    const u32x4 dv = *(const u32x4*)((const uint16_t*)p.dout + dobase + chunk * 8);
-    float acc = 0.0f;
+    float acc = 0.0f, sq = 0.0f;
+    bool live = rh < total_rows;
+    int h = 0;
+    int64_t row = 0;
+    if (live) {
+      h = (int)(rh / p.total_q);
+      row = rh - (int64_t)h * p.total_q;
+      const u32x4 ov = *(const u32x4*)((const uint16_t*)p.o + offs(row, h, p.o_sb, p.o_ss, p.o_sh, p.seqlen_q) + chunk * 8);
+      const u32x4 dv = *(const u32x4*)((const uint16_t*)p.dout + offs(row, h, p.do_sb, p.do_ss, p.do_sh, p.seqlen_q) + chunk * 8);
+      const u32x4 qv = *(const u32x4*)((const uint16_t*)p.q + offs(row, h, p.q_sb, p.q_ss, p.q_sh, p.seqlen_q) + chunk * 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = __builtin_fmaf(bf16_lo(ov[j]), bf16_lo(dv[j]), acc);
-      acc = __builtin_fmaf(bf16_hi(ov[j]), bf16_hi(dv[j]), acc);
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_fmaf(bf16_lo(ov[j]), bf16_lo(dv[j]), acc);
+        acc = __builtin_fmaf(bf16_hi(ov[j]), bf16_hi(dv[j]), acc);
+      }
+      sq = sumsq8(dv);
+      qmax = max(qmax, max_mag8(qv));
     }
 #pragma unroll
-    for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, CPR);
-    if (chunk == 0) p.dvec[(int64_t)h * p.total_q + row] = acc;
+    for (int m = CPR / 2; m >= 1; m >>= 1) {
+      acc += __shfl_xor(acc, m, CPR);
+      sq += __shfl_xor(sq, m, CPR);
+    }
+    if (live && chunk == 0) p.dvec[(int64_t)h * p.total_q + row] = acc;
+    if (live) do2 = fmaxf(do2, sq);
   }
+  uint32_t kmax = 0;
+  float v2 = 0.0f;
+  for (int64_t w = tid; w < ((total_krows * CPR + 63) / 64) * 64; w += nthreads) {
+    const int64_t rh = w / CPR;
+    const int chunk = (int)(w - rh * CPR);
+    float sq = 0.0f;
+    const bool live = rh < total_krows;
+    if (live) {
+      const int h = (int)(rh / p.total_k);
+      const int64_t row = rh - (int64_t)h * p.total_k;
+      const u32x4 kv = *(const u32x4*)((const uint16_t*)p.k + offs(row, h, p.k_sb, p.k_ss, p.k_sh, p.seqlen_k) + chunk * 8);
+      const u32x4 vv = *(const u32x4*)((const uint16_t*)p.v + offs(row, h, p.v_sb, p.v_ss, p.v_sh, p.seqlen_k) + chunk * 8);
+      kmax = max(kmax, max_mag8(kv));
+      sq = sumsq8(vv);
+    }
+#pragma unroll
+    for (int m = CPR / 2; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, CPR);
+    if (live) v2 = fmaxf(v2, sq);
+  }
+  uint32_t* mine = p.stats + 4 + 4 * blockIdx.x;
+  block_max_store(qmax, mine + 0, red);
+  block_max_store(kmax, mine + 1, red);
+  block_max_store(__float_as_uint(do2), mine + 2, red);
+  block_max_store(__float_as_uint(v2), mine + 3, red);
   if (zero_acc) {
     float4* acc4 = (float4*)p.dq_acc;
     const int64_t n4 = total_rows * D / 4;
@@ -123,9 +245,47 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_post: dQ (given layout and dtype) <- fp32 accumulator (already scaled).
+// bwd_convert: Q16 = Q 2^-a and K16 = K 2^-b in [H, rows, D] layout (exact: a bf16 value
+// has 8 significant bits and the fp16 copy 11, and the scaled values stay in fp16's
+// normal range down to 2^-28 of the largest).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_convert_kernel(BwdParams p) {
+  constexpr int CPR = D / 8;
+  const BwdExp ex = bwd_exponents(p);
+  const float sa = pow2f(-ex.a), sb = pow2f(-ex.b);
+  const int64_t nq = (int64_t)p.total_q * p.heads * CPR, nk = (int64_t)p.total_k * p.heads * CPR;
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nq + nk; w += nthreads) {
+    const bool isq = w < nq;
+    const int64_t ww = isq ? w : w - nq;
+    const int64_t rh = ww / CPR;  // row of the [H, rows] layout
+    const int chunk = (int)(ww - rh * CPR);
+    const int rows = isq ? p.total_q : p.total_k;
+    const int h = (int)(rh / rows);
+    const int64_t row = rh - (int64_t)h * rows;
+    int64_t off;
+    if (p.varlen) {
+      off = isq ? row * p.q_ss + h * p.q_sh : row * p.k_ss + h * p.k_sh;
+    } else {
+      const int seqlen = isq ? p.seqlen_q : p.seqlen_k;
+      const int64_t b = row / seqlen, t = row - b * seqlen;
+      off = isq ? b * p.q_sb + t * p.q_ss + h * p.q_sh : b * p.k_sb + t * p.k_ss + h * p.k_sh;
+    }
+    const u32x4 v = *(const u32x4*)((const uint16_t*)(isq ? p.q : p.k) + off + chunk * 8);
+    const float sc = isq ? sa : sb;
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_f16(bf16_lo(v[j]) * sc, bf16_hi(v[j]) * sc);
+    *(u32x4*)((isq ? p.q16 : p.k16) + rh * D + chunk * 8) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_post: dQ (given layout and dtype) <- fp32 accumulator times 2^(f+b).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_post_kernel(BwdParams p) {
+  const BwdExp ex = bwd_exponents(p);
+  const float qs = pow2f(ex.f + ex.b);  // the accumulator holds dQ 2^-(f+b)
   const int64_t total = (int64_t)p.total_q * p.heads * (D / 4);
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += nthreads) {
@@ -140,7 +300,11 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(BwdParams p) {
       const int64_t b = row / p.seqlen_q, s = row - b * p.seqlen_q;
       base = b * p.dq_sb + s * p.dq_ss + h * p.dq_sh;
     }
-    const float4 v = ((const float4*)p.dq_acc)[i];
+    float4 v = ((const float4*)p.dq_acc)[i];
+    v.x *= qs;
+    v.y *= qs;
+    v.z *= qs;
+    v.w *= qs;
     if (p.grad_bf16) {
       u32x2 w = {pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
       *(u32x2*)((uint16_t*)p.dq + base + c4 * 4) = w;
@@ -171,11 +335,11 @@ __device__ __forceinline__ void store_grad4(rsrc_t r, uint32_t byte_off_f32, uin
 // (row reads feed S = Q K^T and dP = dO V^T; transpose reads feed dQ = dS K).
 //
 // Per step and wave:
-//   S = Q K^T, dP = dO V^T       (C layout: lane = key, registers = 16 query rows)
-//   P = 2^(S*c - LSE*log2 e),  dS' = scale * P (dP - D)
-//   dV^T += dO^T P,  dK^T += Q^T [dS'_hi; dS'_lo]   (A operands by transpose reads)
-// Atomic mode: dS'^T (hi, lo) goes to LDS; after a barrier each wave computes one
-// 32x32 block of dQ = dS' K and adds it with fp32 buffer atomics (rows past the end
+//   S = Q16 K16^T (fp16), dP = dO V^T (bf16)   (C layout: lane = key, registers = 16 rows)
+//   P = 2^(S*c 2^(a+b) - LSE*log2 e),  dS16 = scale 2^-f P (dP - D)  (fp16)
+//   dV^T += dO^T P (bf16),  dK^T += Q16^T dS16 (fp16)   (A operands by transpose reads)
+// Atomic mode: dS16^T goes to LDS; after a barrier each wave computes one 32x32 block
+// of dQ 2^-(f+b) = dS16 K16 and adds it with fp32 buffer atomics (rows past the end
 // are dropped by the buffer range check).
 //
 // The Q/dO stage is double-buffered in deterministic mode (the next step streams in
@@ -183,7 +347,7 @@ __device__ __forceinline__ void store_grad4(rsrc_t r, uint32_t byte_off_f32, uin
 // single stage only: its refill is issued after the second barrier (once every wave
 // has finished reading it) and overlaps the dQ part.
 //
-// dS'^T LDS layout: [128 keys][64 queries] bf16, 128-byte rows of sixteen 8-byte
+// dS16^T LDS layout: [128 keys][64 queries] fp16, 128-byte rows of sixteen 8-byte
 // granules; granule g of row r is stored at g ^ ds_swizzle(r), which keeps both the
 // 32-row column writes and the 4-row transpose reads free of bank conflicts.
 __device__ __forceinline__ int ds_swizzle(int row) { return (((row >> 1) & 3) << 2) | ((row >> 3) & 3); }
@@ -210,12 +374,10 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_lds_raw[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds_raw[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char dsh_raw[DQ_ATOMIC ? DS_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char dsl_raw[DQ_ATOMIC ? DS_BYTES : 16];
   auto stage_buf = [&](int st) { return (FA_LDS char*)(st ? stage1 : stage0); };
   FA_LDS char* k_lds = (FA_LDS char*)k_lds_raw;
   FA_LDS char* v_lds = (FA_LDS char*)v_lds_raw;
   FA_LDS char* dsh_lds = (FA_LDS char*)dsh_raw;
-  FA_LDS char* dsl_lds = (FA_LDS char*)dsl_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -243,13 +405,16 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   const int k_blk0 = kblk * BNK;
   if (k_blk0 >= Lk) return;
 
-  const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), do_ss2 = (uint32_t)(p.do_ss * 2);
-  const uint32_t k_ss2 = (uint32_t)(p.k_ss * 2), v_ss2 = (uint32_t)(p.v_ss * 2);
-  const rsrc_t rq = make_rsrc((const uint16_t*)p.q + sq.qoff, rows_bytes(Lq, p.q_ss, ROWB));
+  // Q and K come from their fp16 copies (rows ROWB bytes apart)
+  const uint32_t q_ss2 = (uint32_t)ROWB, do_ss2 = (uint32_t)(p.do_ss * 2);
+  const uint32_t k_ss2 = (uint32_t)ROWB, v_ss2 = (uint32_t)(p.v_ss * 2);
+  const rsrc_t rq = make_rsrc(p.q16 + sq.rowbase * D, (uint32_t)Lq * ROWB);
   const rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + sq.dooff, rows_bytes(Lq, p.do_ss, ROWB));
-  const rsrc_t rk = make_rsrc((const uint16_t*)p.k + sq.koff, rows_bytes(Lk, p.k_ss, ROWB));
+  const rsrc_t rk = make_rsrc(p.k16 + sq.krowbase * D, (uint32_t)Lk * ROWB);
   const rsrc_t rv = make_rsrc((const uint16_t*)p.v + sq.voff, rows_bytes(Lk, p.v_ss, ROWB));
   const rsrc_t racc = make_rsrc(p.dq_acc + (DQ_ATOMIC ? sq.rowbase * D : 0), DQ_ATOMIC ? (uint32_t)Lq * D * 4 : 0u);
+  const BwdExp ex = bwd_exponents(p);
+  const float sc16 = p.scale * pow2f(-ex.f);  // dS16 = sc16 * P (dP - D)
 
   // K and V tiles of the block (rows past the end read as zero)
 #pragma unroll
@@ -266,7 +431,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   const int i_start = CAUSAL ? max(0, k_blk0 - coff) / BM : 0;
   const int i_end = (Lq + BM - 1) / BM;
   const int n_steps = i_end > i_start ? i_end - i_start : 0;
-  const float c = p.scale_log2;
+  const float c = p.scale_log2 * pow2f(ex.a + ex.b);  // S16 = S 2^-(a+b)
 
   auto issue_q = [&](int i, int stage) {
     FA_LDS char* qt = stage_buf(stage);
@@ -333,7 +498,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
     else wait_vmem();
     if (threadIdx.x < BM) {
       lse_l[threadIdx.x] = (lse_next == -INFINITY) ? INFINITY : lse_next * kLog2e;
-      dvec_l[threadIdx.x] = dvec_next * p.scale;
+      dvec_l[threadIdx.x] = dvec_next * sc16;
     }
     __syncthreads();
     if (NSTAGE == 2 && it + 1 < n_steps) {
@@ -347,13 +512,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
     const bool skip = CAUSAL && (k_blk0 + 32 * kw > row0 + 31 + coff);
     bool need_mask = (k_blk0 + BNK > Lk);
     if constexpr (CAUSAL) need_mask = need_mask || (k_blk0 + 32 * kw + 31 > row0 + coff);
-    u32x4 dsh[2], dsl[2];
+    u32x4 dsh[2];
     if (!skip) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int co = ((2 * ds + hl) ^ sw_row) << 4;
-        s = mfma_bf16(lds_read16(qt + arow + co), lds_read16(k_lds + brow + co), s);
+        s = mfma_f16(lds_read16(qt + arow + co), lds_read16(k_lds + brow + co), s);
         dp = mfma_bf16(lds_read16(dot + arow + co), lds_read16(v_lds + brow + co), dp);
       }
       // hidden keys (the causal diagonal, the ragged last block): their scores become
@@ -371,7 +536,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
       u32x4 pb[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        uint32_t ph[4], hh[4], ll[4];
+        uint32_t ph[4], hh[4];
 #pragma unroll
         for (int r4h = 0; r4h < 2; ++r4h) {
           const int r4 = 2 * half + r4h;
@@ -382,21 +547,19 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
           for (int j = 0; j < 4; ++j) {
             const float pe = exp2_hw(__builtin_fmaf(s[4 * r4 + j], c, -l2[j]));
             pv[j] = pe;
-            dsv[j] = pe * __builtin_fmaf(dp[4 * r4 + j], p.scale, -dd[j]);  // scale * P (dP - D)
+            dsv[j] = pe * __builtin_fmaf(dp[4 * r4 + j], sc16, -dd[j]);  // scale 2^-f P (dP - D)
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int k = 2 * r4h + e;
             ph[k] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
-            hh[k] = pack_bf16(dsv[2 * e], dsv[2 * e + 1]);
-            ll[k] = pack_bf16(dsv[2 * e] - bf16_lo(hh[k]), dsv[2 * e + 1] - bf16_hi(hh[k]));
+            hh[k] = pack_f16(dsv[2 * e], dsv[2 * e + 1]);
           }
         }
         pb[half] = u32x4{ph[0], ph[1], ph[2], ph[3]};
         dsh[half] = u32x4{hh[0], hh[1], hh[2], hh[3]};
-        dsl[half] = u32x4{ll[0], ll[1], ll[2], ll[3]};
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS'  (16-row groups of this half)
+      // dV^T += dO^T P ; dK^T += Q16^T dS16  (16-row groups of this half)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int r1 = 32 * qh + 16 * half + tr_r1;
@@ -408,26 +571,23 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
           const u32x2 a_lo = lds_read_tr16(dot + o1), a_hi = lds_read_tr16(dot + o2);
           dvacc[db] = mfma_bf16(u32x4{a_lo[0], a_lo[1], a_hi[0], a_hi[1]}, pb[half], dvacc[db]);
           const u32x2 q_lo = lds_read_tr16(qt + o1), q_hi = lds_read_tr16(qt + o2);
-          const u32x4 qa = u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]};
-          dkacc[db] = mfma_bf16(qa, dsh[half], dkacc[db]);
-          dkacc[db] = mfma_bf16(qa, dsl[half], dkacc[db]);
+          dkacc[db] = mfma_f16(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, dsh[half], dkacc[db]);
         }
       }
     } else {
-      dsh[0] = dsh[1] = dsl[0] = dsl[1] = u32x4{0u, 0u, 0u, 0u};
+      dsh[0] = dsh[1] = u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (DQ_ATOMIC) {
-      // dS'^T to LDS: granule (8qh + 2r4 + hl) of row krow holds rows 32qh + 8r4 + 4hl + 0..3
+      // dS16^T to LDS: granule (8qh + 2r4 + hl) of row krow holds rows 32qh + 8r4 + 4hl + 0..3
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int half = r4 >> 1, e = 2 * (r4 & 1);
         const int off = krow * DS_ROWB + (((8 * qh + 2 * r4 + hl) ^ ds_sw_w) << 3);
         *(FA_LDS u32x2*)(dsh_lds + off) = u32x2{dsh[half][e], dsh[half][e + 1]};
-        *(FA_LDS u32x2*)(dsl_lds + off) = u32x2{dsl[half][e], dsl[half][e + 1]};
       }
     }
     if constexpr (DQ_ATOMIC) {
-      __syncthreads();  // stage consumed by every wave and dS' complete
+      __syncthreads();  // stage consumed by every wave and dS16 complete
       if (it + 1 < n_steps) {
         issue_q(i + 1, 0);
         load_terms(i + 1);
@@ -446,9 +606,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
           const int oa = r1 * DS_ROWB + ((c8 ^ ds_swizzle(r1)) << 3);
           const int ob = (r1 + 8) * DS_ROWB + ((c8 ^ ds_swizzle(r1 + 8)) << 3);
           const u32x2 h1 = lds_read_tr16(dsh_lds + oa), h2 = lds_read_tr16(dsh_lds + ob);
-          const u32x2 l1 = lds_read_tr16(dsl_lds + oa), l2 = lds_read_tr16(dsl_lds + ob);
-          acc = mfma_bf16(u32x4{h1[0], h1[1], h2[0], h2[1]}, kb, acc);
-          acc = mfma_bf16(u32x4{l1[0], l1[1], l2[0], l2[1]}, kb, acc);
+          acc = mfma_f16(u32x4{h1[0], h1[1], h2[0], h2[1]}, kb, acc);
         }
         const uint32_t rowb = (uint32_t)(row0 + 4 * hl) * (D * 4) + (uint32_t)(32 * kw + (lane & 31)) * 4;
 #pragma unroll
@@ -474,6 +632,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
   // ---- sum the two row-half partials of each key group, then store dK, dV ----
   // One 32-column block of d per round through the (now free) K and V buffers:
   // [key group][4 rows of 4][64 lanes] f32x4 each, dK in k_lds and dV in v_lds.
+  const float ks = pow2f(ex.f + ex.a);  // the accumulators hold dK 2^-(f+a)
   const int gb = p.grad_bf16 ? 2 : 4;
   const rsrc_t rdk = make_rsrc((char*)p.dk + sq.dkoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dk_ss * gb) + D * gb : 0u);
   const rsrc_t rdv = make_rsrc((char*)p.dv + sq.dvoff * gb, Lk > 0 ? (uint32_t)(Lk - 1) * (uint32_t)(p.dv_ss * gb) + D * gb : 0u);
@@ -500,8 +659,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
         const int d = 32 * db + 8 * r4 + 4 * hl;
         const f32x4 ok = red_k[r4 * 64 + lane];
         const f32x4 ov = red_v[r4 * 64 + lane];
-        store_grad4(rdk, dk_row + d * 4, dk_row + d * 2, p.grad_bf16, dkacc[db][4 * r4] + ok[0],
-                    dkacc[db][4 * r4 + 1] + ok[1], dkacc[db][4 * r4 + 2] + ok[2], dkacc[db][4 * r4 + 3] + ok[3]);
+        store_grad4(rdk, dk_row + d * 4, dk_row + d * 2, p.grad_bf16, (dkacc[db][4 * r4] + ok[0]) * ks,
+                    (dkacc[db][4 * r4 + 1] + ok[1]) * ks, (dkacc[db][4 * r4 + 2] + ok[2]) * ks,
+                    (dkacc[db][4 * r4 + 3] + ok[3]) * ks);
         store_grad4(rdv, dv_row + d * 4, dv_row + d * 2, p.grad_bf16, dvacc[db][4 * r4] + ov[0],
                     dvacc[db][4 * r4 + 1] + ov[1], dvacc[db][4 * r4 + 2] + ov[2], dvacc[db][4 * r4 + 3] + ov[3]);
       }
@@ -515,9 +675,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
 // Shaped like the forward: eight waves (two per SIMD) of 32 rows each keep Q and
 // dO in registers as B operands; K and V tiles of 64 keys stream through a
 // double-buffered LDS stage.  Per tile and 32-key block:
-//   S^T = K Q^T, dP^T = V dO^T      (lane = query row, registers = keys)
-//   dS'^T = scale * P^T (dP^T - D)  with P^T = 2^(S^T*c - LSE*log2 e)
-//   dQ^T += K^T [dS'_hi; dS'_lo]    (A = K^T by transpose reads)
+//   S^T = K16 Q16^T (fp16), dP^T = V dO^T (bf16)   (lane = query row, registers = keys)
+//   dS16^T = scale 2^-f P^T (dP^T - D)  with P^T = 2^(S^T*c 2^(a+b) - LSE*log2 e)
+//   dQ^T 2^-(f+b) += K16^T dS16^T (fp16)            (A = K16^T by transpose reads)
 // dQ is reduced in registers in a fixed order and written once.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
@@ -562,12 +722,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int wg_q0 = qtile * WG_ROWS;
   if (wg_q0 >= Lq) return;
 
-  const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), do_ss2 = (uint32_t)(p.do_ss * 2);
-  const uint32_t k_ss2 = (uint32_t)(p.k_ss * 2), v_ss2 = (uint32_t)(p.v_ss * 2);
-  const rsrc_t rq = make_rsrc((const uint16_t*)p.q + sq.qoff, rows_bytes(Lq, p.q_ss, ROWB));
+  // Q and K come from their fp16 copies (rows ROWB bytes apart)
+  const uint32_t q_ss2 = (uint32_t)ROWB, do_ss2 = (uint32_t)(p.do_ss * 2);
+  const uint32_t k_ss2 = (uint32_t)ROWB, v_ss2 = (uint32_t)(p.v_ss * 2);
+  const rsrc_t rq = make_rsrc(p.q16 + sq.rowbase * D, (uint32_t)Lq * ROWB);
   const rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + sq.dooff, rows_bytes(Lq, p.do_ss, ROWB));
-  const rsrc_t rk = make_rsrc((const uint16_t*)p.k + sq.koff, rows_bytes(Lk, p.k_ss, ROWB));
+  const rsrc_t rk = make_rsrc(p.k16 + sq.krowbase * D, (uint32_t)Lk * ROWB);
   const rsrc_t rv = make_rsrc((const uint16_t*)p.v + sq.voff, rows_bytes(Lk, p.v_ss, ROWB));
+  const BwdExp ex = bwd_exponents(p);
+  const float sc16 = p.scale * pow2f(-ex.f);  // dS16 = sc16 * P (dP - D)
 
   // rows of this wave: two 128-row tiles interleaved so that the two waves of a
   // SIMD hold neighbouring row blocks
@@ -583,7 +746,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   if (my_row < Lq) {
     const float l = p.lse[sq.lseoff + my_row];
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    dvs = p.dvec[sq.rowbase + my_row] * p.scale;
+    dvs = p.dvec[sq.rowbase + my_row] * sc16;
   }
 
   int kv_end = Lk;
@@ -623,7 +786,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     off_t1[db] = tr_r1 * ROWB + ((cc ^ sw_t1) << 4) + tr_half;
     off_t2[db] = (tr_r1 + 8) * ROWB + ((cc ^ sw_t2) << 4) + tr_half;
   }
-  const float c = p.scale_log2;
+  const float c = p.scale_log2 * pow2f(ex.a + ex.b);  // S16 = S 2^-(a+b)
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -648,13 +811,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        s = mfma_bf16(lds_read16(kt + 32 * kb * ROWB + off_r[ds]), qreg[ds], s);
+        s = mfma_f16(lds_read16(kt + 32 * kb * ROWB + off_r[ds]), qreg[ds], s);
         dp = mfma_bf16(lds_read16(vt + 32 * kb * ROWB + off_r[ds]), doreg[ds], dp);
       }
-      u32x4 dsh[2], dsl[2];
+      u32x4 dsh[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        uint32_t hh[4], ll[4];
+        uint32_t hh[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float dv2[2];
@@ -663,15 +826,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
             const int r = 8 * half + 2 * e + u;
             float pe = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
             if constexpr (MASK) pe = (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) ? 0.0f : pe;
-            dv2[u] = pe * __builtin_fmaf(dp[r], p.scale, -dvs);   // scale * P (dP - D)
+            dv2[u] = pe * __builtin_fmaf(dp[r], sc16, -dvs);   // scale 2^-f P (dP - D)
           }
-          hh[e] = pack_bf16(dv2[0], dv2[1]);
-          ll[e] = pack_bf16(dv2[0] - bf16_lo(hh[e]), dv2[1] - bf16_hi(hh[e]));
+          hh[e] = pack_f16(dv2[0], dv2[1]);
         }
         dsh[half] = u32x4{hh[0], hh[1], hh[2], hh[3]};
-        dsl[half] = u32x4{ll[0], ll[1], ll[2], ll[3]};
       }
-      // dQ^T += K^T dS'^T  (A = K^T through the transpose reads, 16-key groups)
+      // dQ^T += K16^T dS16^T  (A = K16^T through the transpose reads, 16-key groups)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -679,9 +840,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           const int rb = (32 * kb + 16 * half) * ROWB;
           const u32x2 lo = lds_read_tr16(kt + rb + off_t1[db]);
           const u32x2 hi = lds_read_tr16(kt + rb + off_t2[db]);
-          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          dqacc[db] = mfma_bf16(a, dsh[half], dqacc[db]);
-          dqacc[db] = mfma_bf16(a, dsl[half], dqacc[db]);
+          dqacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsh[half], dqacc[db]);
         }
       }
     }
@@ -715,6 +874,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     if (t + 1 < n_tiles) issue_tile(t + 1, (t & 1) ^ 1);
   }
 
+  const float qs = pow2f(ex.f + ex.b);  // the accumulators hold dQ 2^-(f+b)
   const int gb = p.grad_bf16 ? 2 : 4;
   const rsrc_t rdq = make_rsrc((char*)p.dq + sq.dqoff * gb, (uint32_t)(Lq - 1) * (uint32_t)(p.dq_ss * gb) + D * gb);
   const uint32_t row_off = (uint32_t)my_row * (uint32_t)(p.dq_ss * gb);
@@ -723,8 +883,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = 32 * db + 8 * r4 + 4 * hl;
-      store_grad4(rdq, row_off + d * 4, row_off + d * 2, p.grad_bf16, dqacc[db][4 * r4], dqacc[db][4 * r4 + 1],
-                  dqacc[db][4 * r4 + 2], dqacc[db][4 * r4 + 3]);
+      store_grad4(rdq, row_off + d * 4, row_off + d * 2, p.grad_bf16, dqacc[db][4 * r4] * qs,
+                  dqacc[db][4 * r4 + 1] * qs, dqacc[db][4 * r4 + 2] * qs, dqacc[db][4 * r4 + 3] * qs);
     }
 }
 
@@ -771,12 +931,19 @@ static hipError_t launch_bwd_d(const BwdParams& p, int phases, hipStream_t strea
   const bool atomic = !p.deterministic;
   const int64_t rows = (int64_t)p.total_q * p.heads;
   if (phases & 1) {
-    int64_t work = rows * (D / 8);
-    int grid = (int)std::min<int64_t>((work + 255) / 256, 2048 * 4);
+    const int64_t work = std::max(rows, (int64_t)p.total_k * p.heads) * (D / 8);
+    int grid = (int)std::min<int64_t>((work + 255) / 256, kBwdPreBlocks);
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid), dim3(256), 0, stream, p, atomic ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_stats_kernel, dim3(1), dim3(1024), 0, stream, p.stats, grid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t cwork = ((int64_t)p.total_q + p.total_k) * p.heads * (D / 8);
+    int cgrid = (int)std::min<int64_t>((cwork + 255) / 256, 2048 * 4);
+    if (cgrid < 1) cgrid = 1;
+    hipLaunchKernelGGL(bwd_convert_kernel<D>, dim3(cgrid), dim3(256), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // key-block kernel
   if (phases & 2) {

@@ -13,6 +13,7 @@ constexpr int kBwdBlockN = 128;    // keys per backward work item (4 waves x 32 
 constexpr int kBwdBlockM = 64;     // query rows per backward step
 constexpr int kDqTileRows = 256;   // query rows per dQ work item (deterministic mode)
 constexpr int kSchedMaxCost = 8192;  // histogram bins of the longest-first sort
+constexpr int kBwdPreBlocks = 8192;  // most workgroups of the backward's pre pass
 
 struct FwdParams {
   const void* q;
@@ -104,6 +105,21 @@ struct BwdParams {
   float* dq_acc;      // [H, total_q, D] fp32 (fixed length: total_q = B*S_q)
   float* dvec;        // [H, total_q] fp32, D_i = sum_d dO_id O_id
   int32_t* sched;     // variable length work list for the key-tile kernel
+  // fp16 copies of Q and K for the fp16 products (dS enters dK = dS^T Q and dQ = dS K
+  // in fp16, so Q and K must be fp16 there, and S = Q K^T then uses the same copies):
+  // Q16 = Q 2^-a, K16 = K 2^-b, [H, total_q, D] and [H, total_k, D]
+  uint16_t* q16;
+  uint16_t* k16;
+  // maxima found by the pre pass (float bit patterns, so unsigned order = value order):
+  // stats[0..3] = {max |q|, max |k|, max ||dO_i||^2, max ||v_j||^2}, followed by four
+  // per-block slots for each of up to kBwdPreBlocks blocks; the exponents a, b and the
+  // dS exponent f are derived from stats[0..3] by every kernel (bwd_exponents)
+  uint32_t* stats;
+};
+
+// Power-of-two exponents of the backward's fp16 operands, the same in every kernel.
+struct BwdExp {
+  int a, b, f;    // Q16 = Q 2^-a, K16 = K 2^-b, dS16 = dS 2^-f
 };
 
 hipError_t launch_bwd(const BwdParams& p, int phases, hipStream_t stream);  // phases: 1 pre, 2 main, 4 post
