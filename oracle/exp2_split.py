@@ -6,11 +6,11 @@ kernels, which carry their own independently fitted coefficients.
 
 The method (fdeinterviews.com FA4 summary, "Software exponentials" bullet;
 lecompute.fr FA4 article, section "Move some exponential work to different
-units"): compute 2**x on ordinary multiply-add units by splitting x into an
-integer part and a fraction, evaluating a cubic polynomial on the fraction, and
-adding the integer to the exponent field of the resulting float.  After rounding
-to bf16 this agrees with the hardware exponential to within one bf16 unit in the
-last place on 99% of inputs.
+units"): 2**x is formed with multiplies and adds only -- x is split into its
+integer part and its fractional part, a cubic in the fraction approximates 2**f,
+and the integer is added into the float's exponent bits.  The pages state the
+accuracy this reaches against the hardware unit once both are rounded to bf16: a
+difference of at most one bf16 ulp for all but about 1% of arguments.
 
 Readings where the pages leave a step open:
   * the split is floor-based: j = floor(x), f = x - j in [0, 1];

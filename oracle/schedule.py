@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE (only tests/, ``__graft_entry__.smoke()`` and bench.py's
 ``cpu_baseline`` leg may use oracle/).
 
-The method orders its work tiles longest first for causal masks and variable
-lengths (fdeinterviews.com FA4 summary, features paragraph).  A work item is one
+Under a causal mask or with packed sequences of different lengths the work items
+differ in cost, and the method dispatches the most expensive ones first
+(fdeinterviews.com FA4 summary, features paragraph).  A work item is one
 block of ``block_m`` consecutive query rows of one sequence (and one head); its
 length is the number of ``block_n``-key tiles it must visit: all of the
 sequence's key tiles without a mask, and under the causal mask only the tiles

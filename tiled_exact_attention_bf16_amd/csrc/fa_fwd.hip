@@ -6,8 +6,9 @@
 // by tile, and O plus the log-sum-exp are written at the end, so the score matrix
 // never reaches device memory (fdeinterviews.com FA4 summary, opening paragraph;
 // lecompute.fr FA4 article, section "Between the matrix products the kernel must
-// produce weights").  The output is rescaled only when a row maximum grows by more
-// than 8 in log2 units ("Lazy rescaling" bullet), part of the exponentials may run
+// produce weights").  A row's reference maximum -- and with it the accumulated
+// output -- is moved only once the true maximum exceeds it by over 8 in base-2
+// exponent units ("Lazy rescaling" bullet), part of the exponentials may run
 // on the FMA units ("Software exponentials" bullet), two query tiles share each
 // workgroup so one tile's softmax overlaps the other's matrix products ("Pipeline
 // for asynchronous tensor cores" bullet), and work items are dispatched longest

@@ -6,10 +6,11 @@ round-to-nearest-even narrowing of those draws to bfloat16 bit patterns, the
 exact widening of the same bit patterns, and the recipe for variable sequence
 lengths.  Both sides therefore see identical bf16 inputs.
 
-Workloads follow the pages' regime (FlashAttention-4 summary, fdeinterviews.com,
-paragraph on long sequences: gains are largest from 4K tokens up and with causal
-masks; features paragraph: causal masks and variable lengths).  No public dataset
-is named there, so every tensor is drawn i.i.d. from a normal distribution.
+Workloads follow the regime the pages single out (FlashAttention-4 summary,
+fdeinterviews.com, paragraph on long sequences: sequences of several thousand
+tokens, often under a causal mask; features paragraph: causal masks and packed
+batches of different lengths).  The pages name no public dataset, so every tensor
+is drawn i.i.d. from a normal distribution.
 
 Recipe (same for every config):
   rng = numpy.random.default_rng(seed)
