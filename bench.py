@@ -314,6 +314,8 @@ def main():
     ap.add_argument("--tau", type=int, default=-1)
     ap.add_argument("--all-configs", action="store_true",
                     help="also time forward and backward of every named workload (median/min of 50)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other dQ mode's timing and the clock sampling (short profiled runs)")
     ap.add_argument("--workload", default=None,
                     help="only run forward+backward of this named workload (c1..c5, c2_causal, headline) "
                          "--steps times and print per-phase averages (for profiling)")
@@ -361,7 +363,9 @@ def main():
         FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=det, dq=dq, dk=dk, dv=dv, workspace=ws,
                phases=phases)
 
-    clk = ClockSampler().__enter__()
+    clk = ClockSampler() if not args.no_extras else None
+    if clk is not None:
+        clk.__enter__()
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -387,12 +391,13 @@ def main():
     wall = time.perf_counter() - t0
     # the driver's clock readings refresh about every 100 ms: keep sampling through
     # 0.3 s more of the same step, outside the timed region
-    t1 = time.perf_counter()
-    while time.perf_counter() - t1 < 0.3:
-        fwd()
-        bwd()
-        torch.cuda.synchronize()
-    clk.__exit__(None, None, None)
+    if clk is not None:
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < 0.3:
+            fwd()
+            bwd()
+            torch.cuda.synchronize()
+        clk.__exit__(None, None, None)
     if args.copy_calibration:
         # outside the timed region: one copy kernel reading and writing COPY_BYTES
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -449,22 +454,24 @@ def main():
         "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(per[n], 4) for n in names},
         "events_step_ms": round(step_ms, 4),
-        "shader_clock": clk.summary(),
+        "shader_clock": clk.summary() if clk is not None else None,
         "roofline": {"bound": "mfma", "kernel": kernel_names[dominant], "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dominant) if det or dominant == "fwd" else None},
     }
     # the other dQ mode of the same backward, outside the timed step (reported beside it)
     other = not det
+    if args.no_extras:
+        other = None
 
     def bwd_other(phases):
         FA.bwd(do, q, k, v, o, lse, inp.scale, True, deterministic=other, dq=dq, dk=dk, dv=dv, workspace=ws,
                phases=phases)
 
-    for _ in range(args.warmup):
+    for _ in range(args.warmup if other is not None else 0):
         bwd_other(L.FA_BWD_PHASE_ALL)
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps if other is not None else 0)]
+    for i in range(len(ev2)):
         e = ev2[i]
         e[0].record()
         bwd_other(L.FA_BWD_PHASE_PRE)
@@ -474,12 +481,13 @@ def main():
         bwd_other(L.FA_BWD_PHASE_POST)
         e[3].record()
     torch.cuda.synchronize()
-    per2 = {n: float(np.mean([ev2[i][j].elapsed_time(ev2[i][j + 1]) for i in range(args.steps)]))
-            for j, n in enumerate(("bwd_pre", "bwd_main", "bwd_post"))}
-    ms2 = sum(per2.values())
-    out["bwd_" + ("deterministic" if other else "atomic")] = {
-        "ms": round(ms2, 4), "tflops": round(f_bwd / (ms2 * 1e-3) / 1e12, 2),
-        "kernel_ms": {n: round(x, 4) for n, x in per2.items()}}
+    if other is not None:
+        per2 = {n: float(np.mean([ev2[i][j].elapsed_time(ev2[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(("bwd_pre", "bwd_main", "bwd_post"))}
+        ms2 = sum(per2.values())
+        out["bwd_" + ("deterministic" if other else "atomic")] = {
+            "ms": round(ms2, 4), "tflops": round(f_bwd / (ms2 * 1e-3) / 1e12, 2),
+            "kernel_ms": {n: round(x, 4) for n, x in per2.items()}}
     if args.all_configs:
         out["configs"] = time_all_configs(det)
         out["decode"] = time_decode()
