@@ -167,11 +167,13 @@ FwdWs fwd_ws_layout(const Shape& s, int tile_rows, int splits) {
     w.o_off = off;
     off += round_up(rows * s.d * sizeof(float));
   }
-  const size_t krows = (size_t)s.heads * s.total_k;
-  w.v16_off = off;
-  off += round_up(krows * s.d * sizeof(uint16_t));
-  w.vexp_off = off;
-  off += round_up(krows * sizeof(int32_t));
+  if (splits <= 1) {  // the key-split path reads V itself
+    const size_t krows = (size_t)s.heads * s.total_k;
+    w.v16_off = off;
+    off += round_up(krows * s.d * sizeof(uint16_t));
+    w.vexp_off = off;
+    off += round_up(krows * sizeof(int32_t));
+  }
   w.total = off;
   return w;
 }
@@ -286,8 +288,10 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
     p.part_lse = (float*)((char*)workspace + ws.lse_off);
     p.part_o = (float*)((char*)workspace + ws.o_off);
   }
-  p.v16 = (uint16_t*)((char*)workspace + ws.v16_off);
-  p.v_exp = (int32_t*)((char*)workspace + ws.vexp_off);
+  if (splits <= 1) {
+    p.v16 = (uint16_t*)((char*)workspace + ws.v16_off);
+    p.v_exp = (int32_t*)((char*)workspace + ws.vexp_off);
+  }
   fa::FwdConfig cfg{s.d, c.qt, a->causal != 0, s.varlen, c.poly, c.tau, splits};
   hipStream_t strm = (hipStream_t)stream;
   if (s.varlen) {
@@ -295,7 +299,7 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
                                            (int32_t*)workspace, strm);
     if (e != hipSuccess) return FA_ERR_HIP;
   }
-  if (s.total_k > 0 && fa::launch_fwd_vprep(p, s.d, s.varlen, strm) != hipSuccess) return FA_ERR_HIP;
+  if (splits <= 1 && s.total_k > 0 && fa::launch_fwd_vprep(p, s.d, s.varlen, strm) != hipSuccess) return FA_ERR_HIP;
   return fa::launch_fwd(p, cfg, strm) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

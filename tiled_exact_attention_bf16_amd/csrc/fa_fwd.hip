@@ -50,6 +50,15 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   constexpr int NKB = BN / 32;                // 32-key blocks per tile
   constexpr int NDS = D / 16;                 // k-steps of the QK product
   constexpr int NDB = D / 32;                 // 32-wide blocks of head_dim
+  // The main path forms fp16 weights against the fp16 copy of V (the lazy reference
+  // leaves weights up to 2^8, which bf16 would round too coarsely).  The key-split path
+  // serves short query blocks against long keys, where reading K and V bounds the time
+  // and an fp16 copy of V would double V's traffic: it reads V itself, with bf16
+  // weights and eager rescaling (every row's largest weight stays exactly 1, and a
+  // rescale costs nothing there).  With the largest weight exactly 1 the others'
+  // bf16 rounding stays small against the sum, so it normalises O and forms the LSE
+  // from the fp32 weights' sum.
+  constexpr bool F16 = !SPLIT;
   // Two K buffers and two V buffers (K runs one tile ahead of V), declared as
   // separate objects: the compiler can then tell that the buffers a step reads are
   // not the ones its DMA loads are filling, and does not make the reads wait for
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     h = bh - b * p.heads;
   }
   int Lq = p.seqlen_q, Lk = p.seqlen_k;
-  int64_t qoff, koff, ooff, lseoff;
+  int64_t qoff, koff, voff, ooff, lseoff;
   int64_t krow0;  // first key row of the sequence among all key rows (the fp16 V copy's rows)
   if constexpr (VARLEN) {
     const int sq = p.cu_q[b], sk = p.cu_k[b];
@@ -92,12 +101,14 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     Lk = p.cu_k[b + 1] - sk;
     qoff = sq * p.q_ss + h * p.q_sh;
     koff = sk * p.k_ss + h * p.k_sh;
+    voff = sk * p.v_ss + h * p.v_sh;
     ooff = sq * p.o_ss + h * p.o_sh;
     lseoff = (int64_t)h * p.total_q + sq;
     krow0 = sk;
   } else {
     qoff = b * p.q_sb + h * p.q_sh;
     koff = b * p.k_sb + h * p.k_sh;
+    voff = b * p.v_sb + h * p.v_sh;
     ooff = b * p.o_sb + h * p.o_sh;
     lseoff = ((int64_t)b * p.heads + h) * Lq;
     krow0 = (int64_t)b * Lk;
@@ -115,18 +126,20 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const int per = (tiles + p.n_split - 1) / p.n_split;
     const int kbase = min(chunk * per, tiles) * kFwdBlockN;
     koff += (int64_t)kbase * p.k_ss;
+    voff += (int64_t)kbase * p.v_ss;
     krow0 += kbase;
     Lk = max(0, min(Lk - kbase, per * kFwdBlockN));
     coff -= kbase;
   }
 
   const uint32_t q_ss2 = (uint32_t)(p.q_ss * 2), k_ss2 = (uint32_t)(p.k_ss * 2);
-  const uint32_t v_ss2 = (uint32_t)ROWB, o_ss2 = (uint32_t)(p.o_ss * 2);
+  const uint32_t v_ss2 = F16 ? (uint32_t)ROWB : (uint32_t)(p.v_ss * 2), o_ss2 = (uint32_t)(p.o_ss * 2);
   const rsrc_t rq = make_rsrc((const char*)p.q + qoff * 2, (uint32_t)(Lq - 1) * q_ss2 + ROWB);
   const rsrc_t rk = make_rsrc((const char*)p.k + koff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * k_ss2 + ROWB : 0u);
   // the fp16 copy of V: rows of this (sequence, head) are contiguous, ROWB bytes apart
   const int64_t vrow = (int64_t)h * p.total_k + krow0;
-  const rsrc_t rv = make_rsrc(p.v16 + vrow * D, Lk > 0 ? (uint32_t)Lk * ROWB : 0u);
+  const rsrc_t rv = F16 ? make_rsrc(p.v16 + vrow * D, Lk > 0 ? (uint32_t)Lk * ROWB : 0u)
+                        : make_rsrc((const char*)p.v + voff * 2, Lk > 0 ? (uint32_t)(Lk - 1) * v_ss2 + ROWB : 0u);
   // tile j's exponent at v_exp[j * BN], read through the constant address space so that
   // it is a scalar load: a vector load would share vmcnt with the K/V DMA loads, and
   // waiting for it would wait for them
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   // products used.  O is normalised by it, so a dominant weight's rounding cancels
   // between numerator and denominator; and since every weight rounds with relative
   // error <= 2^-11, ln of it is within 4.9e-4 of ln of the exact sum.
-  float lsum_r = 0.0f;
+  float lsum_r = 0.0f;  // main path: sum of the rounded weights; key-split path: fp32 sum
   const float c = p.scale_log2;
 
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const FA_LDS char* vt = vbuf(PAR ^ 1);
     const int k0 = j * BN;
     int e_cur = 0;  // power-of-two exponent of tile j's fp16 V copy (wave-uniform)
-    if constexpr (NEXT) e_cur = v_exp[k0];
+    if constexpr (NEXT && F16) e_cur = v_exp[k0];
 
     // -- phase 1: S(j)'s MFMAs, with the exponentials of tile j-1's first 32-key
     // block (with their fp16 packing) between them.  The second block's
@@ -223,6 +236,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // the first block's weights: the vector work (an exponential costs four FMA
     // issue slots) is then spread over 24 of the step's 32 MFMAs instead of 16 --
     u32x4 pb[2 * NKB];
+    float rs[2] = {0.0f, 0.0f};  // key-split path: fp32 sums
     auto exp_pair = [&](const int q) {  // scores 2u, 2u+1 of block kb = q / 8 of tile j-1
       const int kb = q >> 3, u = q & 7, e = 2 * u;
       // P' = 2^(s*c - m*c + e) = P 2^e -> fp16 operands
@@ -230,7 +244,12 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       const float x1 = __builtin_fmaf(s_prev[kb][e + 1], c, -mref_x);
       const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
       const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
-      pb[2 * kb + (u >> 2)][u & 3] = pack_f16(p0, p1);
+      if constexpr (F16) {
+        pb[2 * kb + (u >> 2)][u & 3] = pack_f16(p0, p1);
+      } else {
+        pb[2 * kb + (u >> 2)][u & 3] = pack_bf16(p0, p1);
+        rs[u & 1] += p0 + p1;
+      }
     };
     constexpr int NPAIR = 8 * NKB;   // pairs of scores per lane and tile
     constexpr int P1 = 8;            // pairs of phase 1: the first block
@@ -296,7 +315,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
             exp_pair(q);
           const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
           const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
-          oacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
+          if constexpr (F16) oacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
+          else oacc[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
           if constexpr (NEXT) {
             // two scores of S(j) per MFMA, 32 in all
 #pragma unroll
@@ -311,7 +331,9 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int g = 0; g < BN / 16; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rsr[e & 1] = add_f16_pair(pb[g][e], rsr[e & 1]);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (F16) rsr[e & 1] = add_f16_pair(pb[g][e], rsr[e & 1]);
+        }
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
       for (int i = 0; i < NM2 / 2; ++i) {
@@ -327,7 +349,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       }
       // the empty asm makes the sums exist here, so their adds are scheduled among
       // this phase's MFMAs instead of being sunk past the rescale branch
-      lsum_r += (rsr[0] + rsr[1]) * esc;
+      if constexpr (F16) lsum_r += (rsr[0] + rsr[1]) * esc;
+      else lsum_r += rs[0] + rs[1];
       asm volatile("" : "+v"(lsum_r));
       __builtin_amdgcn_sched_barrier(0);
     } else if constexpr (NEXT) {
@@ -346,7 +369,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       mx = half_swap_max(mx);
       const float m_new = fmaxf(m_used, mx);
       bool need = m_new > m_used;
-      if constexpr (TAU > 0) {
+      if constexpr (TAU > 0 && F16) {
         const float tau = e_cur > 7 ? 0.0f : (float)TAU;
         need = need && (m_used == -INFINITY || (m_new - m_used) * c > tau);
       }
@@ -640,7 +663,8 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream, int max_ite
   if (grid == 0) return hipSuccess;
   if constexpr (NQT == 1) {
     if (p.n_split > 1) {
-      hipLaunchKernelGGL((fwd_kernel<D, 1, CAUSAL, VARLEN, POLY, TAU, true>), dim3(grid * (unsigned)p.n_split),
+      // the key-split kernel rescales eagerly (tau = 0; see F16 in fwd_kernel)
+      hipLaunchKernelGGL((fwd_kernel<D, 1, CAUSAL, VARLEN, POLY, 0, true>), dim3(grid * (unsigned)p.n_split),
                          dim3(256), 0, stream, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
