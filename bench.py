@@ -64,8 +64,10 @@ def recorded_traffic(phase: str):
 
 class ClockSampler:
     """Shader clock while the kernels run: amdsmi's current GFX clock of each of the
-    GPU's XCDs (gpu metrics), read every 5 ms by a background thread; readings taken
-    while the GPU idled (below 500 MHz, deep sleep) are dropped.  None without amdsmi."""
+    GPU's XCDs (gpu metrics), polled every 5 ms by a background thread; each new
+    reading (the driver refreshes them far less often than that) counts once, and
+    readings of an idle GPU (below 500 MHz, deep sleep) are dropped.  None without
+    amdsmi."""
 
     def __init__(self):
         import threading
@@ -83,12 +85,15 @@ class ClockSampler:
             self.ok = False
 
     def _run(self):
+        last = None
         while not self._stop.is_set():
             try:
                 cur = self._smi.amdsmi_get_gpu_metrics_info(self._h).get("current_gfxclks")
                 vals = [float(x) for x in cur if isinstance(x, (int, float)) and 0 < x < 10000]
-                if vals and min(vals) >= 500:
-                    self.mhz.append(sum(vals) / len(vals))
+                if vals and vals != last:
+                    last = vals
+                    if min(vals) >= 500:
+                        self.mhz.append(sum(vals) / len(vals))
             except Exception:
                 pass
             time.sleep(0.005)
@@ -108,8 +113,8 @@ class ClockSampler:
             return None
         return {"mean_mhz": round(float(np.mean(self.mhz)), 1), "min_mhz": round(min(self.mhz), 1),
                 "max_mhz": round(max(self.mhz), 1), "samples": len(self.mhz),
-                "source": "amdsmi current_gfxclks (mean over XCDs), every 5 ms from warm-up through 0.3 s "
-                          "of the same step after the timed region"}
+                "source": "amdsmi current_gfxclks (mean over XCDs), each new reading from warm-up until "
+                          "three busy readings arrived while the same step kept running after the timed region"}
 
 
 def cpu_model() -> str:
@@ -389,11 +394,12 @@ def main():
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the driver's clock readings refresh about every 100 ms: keep sampling through
-    # 0.3 s more of the same step, outside the timed region
+    # the driver refreshes its clock readings only every few hundred ms and a short
+    # timed region can end before one shows the busy clock: keep running the same step
+    # outside the timed region until three busy readings have arrived, for at most 4 s
     if clk is not None:
         t1 = time.perf_counter()
-        while time.perf_counter() - t1 < 0.3:
+        while time.perf_counter() - t1 < 4.0 and len(clk.mhz) < 3:
             fwd()
             bwd()
             torch.cuda.synchronize()

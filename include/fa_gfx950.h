@@ -125,11 +125,11 @@ typedef struct fa_fwd_tuning {
 
 /* Bytes of device workspace fa_fwd needs for `a` and `tuning` (NULL = defaults):
  * room for the longest-first work list of variable-length batches (fdeinterviews.com
- * FA4 summary, features paragraph), for the partial results of a key split, and for
- * an fp16 copy of V with one power-of-two exponent per 64-key tile (2 bytes per V
- * element plus 4 bytes per key row and head): the PV product runs in fp16, so that
- * the weights keep 11 significant bits under the lazy reference.  0 only for an
- * empty problem.  Validates `a` and `tuning` exactly as fa_fwd does and
+ * FA4 summary, features paragraph), and either for the partial results of a key
+ * split (fp32 O and LSE per chunk) or, without a split, for an fp16 copy of V with
+ * one power-of-two exponent per 64-key tile (2 bytes per V element plus 4 bytes per
+ * key row and head): the unsplit PV product runs in fp16, so that the weights keep
+ * 11 significant bits under the lazy reference.  0 only for an empty problem.  Validates `a` and `tuning` exactly as fa_fwd does and
  * returns the same status; `bytes` must not be NULL (FA_ERR_INVALID_ARGUMENT).  No
  * HIP call is made. */
 fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tuning, size_t* bytes);
@@ -221,8 +221,10 @@ typedef struct fa_bwd_args {
 } fa_bwd_args;
 
 /* Bytes of device workspace fa_bwd needs for `a`: the fp32 dQ accumulator (atomic
- * mode only), the row terms D_i = sum_d dO_id O_id and the work lists of
- * variable-length batches.  Validates `a` exactly as fa_bwd does and returns the
+ * mode only), the row terms D_i = sum_d dO_id O_id, the fp16 copies of Q and K that
+ * the dS products use (2 * head_dim bytes per query row and per key row, per head),
+ * the pre pass's magnitude maxima (128 KiB) and the work lists of variable-length
+ * batches.  Validates `a` exactly as fa_bwd does and returns the
  * same status; `bytes` must not be NULL.  No HIP call is made. */
 fa_status fa_bwd_workspace_size(const fa_bwd_args* a, size_t* bytes);
 
@@ -262,9 +264,11 @@ fa_status fa_bwd_phases(const fa_bwd_args* a, int32_t phases, void* workspace, s
  * array inside the library (fa_bwd_noalloc_scratch_bytes() bytes, 64 MiB, one copy
  * per GPU, held until the process ends); the call allocates nothing.  A request whose
  * workspace (fa_bwd_workspace_size) exceeds that size returns
- * FA_ERR_WORKSPACE_TOO_SMALL before any device work: the deterministic mode needs
- * 4 bytes per query row and head (plus the work lists of variable-length batches),
- * the atomic mode 4 * (head_dim + 1) bytes per query row and head.  Every call on a
+ * FA_ERR_WORKSPACE_TOO_SMALL before any device work: per head the deterministic
+ * mode needs 4 + 2 * head_dim bytes per query row and 2 * head_dim bytes per key row,
+ * plus 128 KiB and the work lists of variable-length batches; the atomic mode adds
+ * 4 * head_dim bytes per query row and head (e.g. B=1 S=4096 H=16 d=128 fits
+ * deterministically, B=2 S=8192 does not).  Every call on a
  * GPU uses that GPU's one array, whose contents carry over from the last call (each
  * call writes everything it reads): calls that overlap in time on one GPU -- on
  * different streams, or from different threads -- race and give undefined
