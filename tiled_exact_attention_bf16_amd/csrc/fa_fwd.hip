@@ -31,7 +31,13 @@
 //     factor 2^e back (it is folded into the exponent argument), so P'V' = PV;
 //     V^T comes from ds_read_b64_tr_b16 transpose reads;
 //   * the O^T accumulators also hold one query row per lane, so the rescale factor
-//     is a per-lane scalar.
+//     is a per-lane scalar;
+//   * with two query tiles per workgroup (the default) the tiles run in ping-pong:
+//     wave w (first tile) and wave w+4 (second tile) share a SIMD, and in each half
+//     step one of them issues the step's 32 MFMAs while the other forms its weights,
+//     so that the vector work runs beside matrix products of the other wave.  The
+//     row sum there is a plain fp32 sum: v_dot2 executes on the matrix pipeline and
+//     would wait behind the other wave's MFMAs.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -59,6 +65,10 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   // bf16 rounding stays small against the sum, so it normalises O and forms the LSE
   // from the fp32 weights' sum.
   constexpr bool F16 = !SPLIT;
+  // two query tiles per workgroup run in ping-pong (one tile's matrix products beside
+  // the other's weights); one tile per workgroup and the key split pipeline each
+  // wave's own step instead
+  constexpr bool PP = NQT == 2 && !SPLIT;
   // Two K buffers and two V buffers (K runs one tile ahead of V), declared as
   // separate objects: the compiler can then tell that the buffers a step reads are
   // not the ones its DMA loads are filling, and does not make the reads wait for
@@ -194,11 +204,12 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   float mref = 0.0f;    // m_used * c once a row has seen a key
   float mref_x = 0.0f;  // mref - e of the tile whose weights are formed next (weights carry 2^e)
   float esc = 1.0f;     // 2^-e of that tile: its weight sums back in true units
-  // One row sum serves both O and LSE: the sum of the fp16-rounded weights the PV
-  // products used.  O is normalised by it, so a dominant weight's rounding cancels
-  // between numerator and denominator; and since every weight rounds with relative
-  // error <= 2^-11, ln of it is within 4.9e-4 of ln of the exact sum.
-  float lsum_r = 0.0f;  // main path: sum of the rounded weights; key-split path: fp32 sum
+  // One row sum serves both O and LSE.  The ping-pong path and the key-split path
+  // sum the fp32 weights.  The one-tile path sums the fp16-rounded weights the PV
+  // products used: O normalised by it has a dominant weight's rounding cancel between
+  // numerator and denominator, and since every weight rounds with relative error
+  // <= 2^-11, ln of it is within 4.9e-4 of ln of the exact sum.
+  float lsum_r = 0.0f;
   const float c = p.scale_log2;
 
   // Under the causal mask a wave's rows stop seeing keys before the workgroup's
@@ -398,6 +409,215 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   int j_plain = Lk / BN;
   if constexpr (CAUSAL) j_plain = min(j_plain, max(0, q0 + 1 + coff) / BN);
   const int j_lim = min(n_mine, j_plain);
+  if constexpr (PP) {
+    // ---- two query tiles in ping-pong.  The workgroup's two 128-row tiles run half a
+    // step apart: a step is two slots between workgroup barriers, and in each slot
+    // one tile's waves issue the matrix products while the other tile's waves, on the
+    // same SIMDs (wave w and wave w+4 share one), form the weights of their last
+    // scores.  The lead tile (waves 0-3) runs M(m) in slot 2m and V(m) in slot 2m+1;
+    // the lag tile runs V(m-1) in slot 2m and M(m) in slot 2m+1.  K(m+1) and V(m) are
+    // loaded from slot 2m on and waited for at the barrier that opens slot 2m+2;
+    // K(j) sits in K buffer j&1, V(j) in V buffer j&1. ----
+    const bool lead = (wave >> 2) == 0;
+    f32x16 s[NKB];      // S(j) of the tile in hand
+    u32x4 pb[2 * NKB];  // its fp16 weights, the B operand of the next PV product
+    static_assert(NKB * NDS == (BN / 16) * NDB, "S and PV products pair up");
+    // matrix slot of tile j: S(j) = K(j) Q^T (DS) and O^T += V(j-1)^T P(j-1)^T (DPV).
+    // The wave's priority is raised so that its MFMAs issue as soon as the matrix
+    // core is free.
+    auto mphase = [&](auto par_c, auto ds_c, auto dpv_c) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_c)::value;  // j & 1
+      constexpr bool DS = decltype(ds_c)::value, DPV = decltype(dpv_c)::value;
+      const FA_LDS char* kt = kbuf(P);
+      const FA_LDS char* vt = vbuf(P ^ 1);
+      if constexpr (DS || DPV) __builtin_amdgcn_s_setprio(1);
+      if constexpr (DS) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+      }
+      // S and PV products alternate, so that no MFMA waits for the one before it
+#pragma unroll
+      for (int i = 0; i < NKB * NDS; ++i) {
+        if constexpr (DS) {
+          const int kb = i & 1, ds = i >> 1;
+          const u32x4 a = lds_read16(kt + 32 * kb * ROWB + off_k[ds]);
+          s[kb] = mfma_bf16(a, qreg[ds], s[kb]);
+        }
+        if constexpr (DPV) {
+          const int g = i / NDB, db = i % NDB;
+          const u32x2 lo = lds_read_tr16(vt + 16 * g * ROWB + off_v1[db]);
+          const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
+          oacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
+        }
+      }
+      if constexpr (DS || DPV) {
+        // operand reads run a few MFMAs ahead
+        constexpr int NMF = (DS ? NKB * NDS : 0) + (DPV ? (BN / 16) * NDB : 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    // fp16 weights P' = 2^(s c - mx_ref) of the tile in hand, and the fp32 sum of the
+    // unrounded weights (plain adds: v_dot2 runs on the matrix pipeline and would wait
+    // behind the other wave's MFMAs)
+    float wsum[2];
+    auto weights = [&](const float mx_ref) __attribute__((always_inline)) {
+      wsum[0] = wsum[1] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8 * NKB; ++q) {
+        const int kb = q >> 3, u = q & 7, e = 2 * u;
+        const float x0 = __builtin_fmaf(s[kb][e], c, -mx_ref);
+        const float x1 = __builtin_fmaf(s[kb][e + 1], c, -mx_ref);
+        const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
+        const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
+        pb[2 * kb + (u >> 2)][u & 3] = pack_f16(p0, p1);
+        wsum[q & 1] += p0 + p1;
+      }
+    };
+    // vector slot of tile j: mask; weights against the current reference, formed
+    // before the row maximum is known (they stand unless the maximum moves the
+    // reference, which the lazy threshold makes rare, and are redone then); row
+    // maximum as four independent chains; lazy rescale; row sum
+    auto vphase = [&](const int j, auto mask_c) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const int k0 = j * BN;
+      const int e_cur = v_exp[k0];  // tile j's V-copy exponent: weights carry 2^e_cur
+      if constexpr (MASK) {
+        int lim = Lk;
+        if constexpr (CAUSAL) lim = min(lim, my_row + 1 + coff);
+        lim -= k0 + 4 * hl;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = rel >= lim ? -INFINITY : s[kb][r];
+          }
+      }
+      weights(mref - (float)e_cur);
+      float mp[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, r0 = 8 * (t & 1);
+        mp[t] = max3(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2]);
+        mp[t] = max3(mp[t], s[kb][r0 + 3], s[kb][r0 + 4]);
+        mp[t] = max3(mp[t], s[kb][r0 + 5], s[kb][r0 + 6]);
+        mp[t] = fmaxf(mp[t], s[kb][r0 + 7]);
+      }
+      float mx = max3(mp[0], mp[1], fmaxf(mp[2], mp[3]));
+      mx = half_swap_max(mx);
+      // lazy rescale: move the reference only when the maximum grew by more than TAU
+      // (every growth on a tile whose V copy needed e > 7, so that P 2^e fits fp16)
+      const float m_new = fmaxf(m_used, mx);
+      bool need = m_new > m_used;
+      if constexpr (TAU > 0) {
+        const float tau = e_cur > 7 ? 0.0f : (float)TAU;
+        need = need && (m_used == -INFINITY || (m_new - m_used) * c > tau);
+      }
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? (m_used == -INFINITY ? 0.0f : exp2_hw((m_used - m_new) * c)) : 1.0f;
+        m_used = need ? m_new : m_used;
+        mref = (m_used == -INFINITY) ? 0.0f : m_used * c;
+        lsum_r *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        weights(mref - (float)e_cur);
+      }
+      lsum_r += (wsum[0] + wsum[1]) * __int_as_float((127 - e_cur) << 23);
+    };
+    // opening of step m (slot 2m): wait for the loads issued at slot 2m-2, barrier,
+    // start K(m+1) and V(m)
+    auto open_step = [&](const int m, auto par_c) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_c)::value;
+      wait_vmem();
+      __syncthreads();
+      if (m + 1 < n_tiles) issue(rk, k_ss2, m + 1, kbuf(P ^ 1));
+      if (m < n_tiles) issue(rv, v_ss2, m, vbuf(P));
+    };
+    // Steps come in kinds fixed at compile time (which products and weights a wave
+    // has in them, whether the tile needs the mask), run from straight-line
+    // sequences: branching on the kind inside one loop makes the register allocator
+    // copy the accumulators between the paths.
+    auto lead_step = [&](const int m, auto par_c, auto ds_c, auto dpv_c, auto v_c, auto mask_c)
+                         __attribute__((always_inline)) {
+      open_step(m, par_c);
+      mphase(par_c, ds_c, dpv_c);
+      __syncthreads();
+      if constexpr (decltype(v_c)::value) vphase(m, mask_c);
+    };
+    auto lag_step = [&](const int m, auto par_c, auto v_c, auto mask_c, auto ds_c, auto dpv_c)
+                        __attribute__((always_inline)) {
+      open_step(m, par_c);
+      if constexpr (decltype(v_c)::value) vphase(m - 1, mask_c);
+      __syncthreads();
+      mphase(par_c, ds_c, dpv_c);
+    };
+    // A wave with n = n_mine tiles: step 0 has S(0) and (lead) its weights; steps
+    // 1..n-1 have everything; step n has PV(n-1) (and, lag, the weights of n-1);
+    // steps past n only load and keep the barriers.  Weights of tile j are masked
+    // from j_plain on.  Every wave runs steps 0..n_tiles, two barriers each.
+    const int n = n_mine, jl = min(n_mine, j_plain);
+    if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
+    int m = 0;
+    if (lead) {
+      if (n > 0) {
+        lead_step(0, I0{}, BT{}, BF{}, BT{}, MT{});
+        m = 1;
+        for (; m + 1 < jl; m += 2) {  // m odd
+          lead_step(m, I1{}, BT{}, BT{}, BT{}, MF{});
+          lead_step(m + 1, I0{}, BT{}, BT{}, BT{}, MF{});
+        }
+        for (; m + 1 < n; m += 2) {
+          lead_step(m, I1{}, BT{}, BT{}, BT{}, MT{});
+          lead_step(m + 1, I0{}, BT{}, BT{}, BT{}, MT{});
+        }
+        if (m < n) {  // m = n - 1: tile m, then PV(m) alone
+          lead_step(m, I1{}, BT{}, BT{}, BT{}, MT{});
+          lead_step(m + 1, I0{}, BF{}, BT{}, BF{}, MF{});
+          m += 2;
+        } else {      // m = n
+          lead_step(m, I1{}, BF{}, BT{}, BF{}, MF{});
+          m += 1;
+        }
+      }
+      for (; m <= n_tiles; ++m) {
+        if (m & 1) lead_step(m, I1{}, BF{}, BF{}, BF{}, MF{});
+        else lead_step(m, I0{}, BF{}, BF{}, BF{}, MF{});
+      }
+    } else {
+      if (n > 0) {
+        lag_step(0, I0{}, BF{}, MF{}, BT{}, BF{});
+        m = 1;
+        for (; m < jl && m + 1 < n; m += 2) {  // m odd; V(m-1), V(m) unmasked
+          lag_step(m, I1{}, BT{}, MF{}, BT{}, BT{});
+          lag_step(m + 1, I0{}, BT{}, MF{}, BT{}, BT{});
+        }
+        for (; m + 1 < n; m += 2) {
+          lag_step(m, I1{}, BT{}, MT{}, BT{}, BT{});
+          lag_step(m + 1, I0{}, BT{}, MT{}, BT{}, BT{});
+        }
+        if (m < n) {  // m = n - 1
+          lag_step(m, I1{}, BT{}, MT{}, BT{}, BT{});
+          lag_step(m + 1, I0{}, BT{}, MT{}, BF{}, BT{});
+          m += 2;
+        } else {      // m = n
+          lag_step(m, I1{}, BT{}, MT{}, BF{}, BT{});
+          m += 1;
+        }
+      }
+      for (; m <= n_tiles; ++m) {
+        if (m & 1) lag_step(m, I1{}, BF{}, MF{}, BF{}, BF{});
+        else lag_step(m, I0{}, BF{}, MF{}, BF{}, BF{});
+      }
+    }
+  } else {
   f32x16 sa[NKB], sb[NKB];
   if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
   int j = 0;
@@ -429,6 +649,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     const int par = j & 1;
     if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(par ^ 1));
     if (j < n_tiles) issue(rv, v_ss2, j, vbuf(par));
+  }
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l (O_acc and the sums are in
