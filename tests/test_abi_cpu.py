@@ -31,6 +31,12 @@ def test_every_declared_symbol_is_exported():
     assert set(L.SIGNATURES) == set(names)
 
 
+def test_check_build_exports_the_same_symbols():
+    serial = L.load(L.SERIAL_LIB_PATH)  # the serial-loads check build
+    for n in declared_functions():
+        assert hasattr(serial, n), n
+
+
 def test_status_strings():
     for code, name in [(0, "FA_OK"), (1, "FA_ERR_INVALID_ARGUMENT"), (2, "FA_ERR_UNSUPPORTED"),
                        (3, "FA_ERR_WORKSPACE_TOO_SMALL"), (4, "FA_ERR_HIP")]:

@@ -10,6 +10,8 @@ import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_gfx950.so")
+# check build: every buffer->LDS load batch waited for as soon as it is issued
+SERIAL_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_gfx950_serial.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARGUMENT = 1
@@ -87,20 +89,25 @@ SIGNATURES = {
 }
 
 
+def load(path: str):
+    """A handle on the library at `path` with every entry point's signature set."""
+    if not os.path.exists(path):
+        raise FaLibraryMissing(
+            f"{path} is not built; run `python -m tiled_exact_attention_bf16_amd.build_lib` "
+            "(there is no fallback implementation)")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
     """The loaded library (built in place by build_lib.py); raises if it is missing."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise FaLibraryMissing(
-                f"{LIB_PATH} is not built; run `python -m tiled_exact_attention_bf16_amd.build_lib` "
-                "(there is no fallback implementation)")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
 
 

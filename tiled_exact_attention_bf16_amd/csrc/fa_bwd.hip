@@ -425,6 +425,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
     buf_load_lds16(rk, k_lds + i * 1024, (uint32_t)(k_blk0 + r) * k_ss2 + cc * 16);
     buf_load_lds16(rv, v_lds + i * 1024, (uint32_t)(k_blk0 + r) * v_ss2 + cc * 16);
   }
+  dma_issued();
 
   // causal: row i sees keys j <= i + coff (bottom-right alignment; 0 for equal lengths)
   const int coff = Lk - Lq;
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdParams p) {
       buf_load_lds16(rq, qt + j * 1024, (uint32_t)(i * BM + r) * q_ss2 + cc * 16);
       buf_load_lds16(rdo, dot + j * 1024, (uint32_t)(i * BM + r) * do_ss2 + cc * 16);
     }
+    dma_issued();
   };
   float lse_next = 0.0f, dvec_next = 0.0f;
   auto load_terms = [&](int i) {
@@ -768,6 +770,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       buf_load_lds16(rk, kd + i * 1024, (uint32_t)(k0 + r) * k_ss2 + cc * 16);
       buf_load_lds16(rv, vd + i * 1024, (uint32_t)(k0 + r) * v_ss2 + cc * 16);
     }
+    dma_issued();
   };
 
   // lane-constant LDS offsets within a tile: with the stage a compile-time constant

@@ -67,6 +67,16 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Called after every batch of buffer->LDS loads.  A check build (FA_SERIAL_LOADS)
+// waits for the batch right there, so that no load overlaps the computation; its
+// results must equal the normal build's bit for bit, which they do only if no
+// computation reads LDS that a load in flight is still filling.
+__device__ __forceinline__ void dma_issued() {
+#ifdef FA_SERIAL_LOADS
+  wait_vmem();
+#endif
+}
+
 // s_waitcnt vmcnt(16): vector memory operations retire in issue order, so this
 // waits for everything but the 16 most recent ones (e.g. fire-and-forget atomics
 // issued after a stage's loads).

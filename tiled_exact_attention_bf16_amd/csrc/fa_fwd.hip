@@ -177,6 +177,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       const int cs = (idx % SLOTS) ^ slot_swizzle<D>(r);
       buf_load_lds16(rsrc, dst + i * 1024, (uint32_t)(k0 + r) * ss2 + cs * 16);
     }
+    dma_issued();
   };
 
   // lane-constant LDS offsets within a tile buffer: with the buffer index a
