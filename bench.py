@@ -117,6 +117,16 @@ class ClockSampler:
                           "three busy readings arrived while the same step kept running after the timed region"}
 
 
+def at_clock(clock, step_tf: float, fwd_tf: float, bwd_tf: float):
+    """The same rates against the MFMA peak at the shader clock measured during the run
+    (the 2.5 PFLOP/s figure assumes 2.4 GHz; these kernels run the chip well below)."""
+    if not clock:
+        return None
+    peak = PEAK_BF16_TFLOPS * clock["mean_mhz"] / 2400.0
+    return {"peak_tflops": round(peak, 1), "frac_of_peak": round(step_tf / peak, 4),
+            "fwd_frac_of_peak": round(fwd_tf / peak, 4), "bwd_frac_of_peak": round(bwd_tf / peak, 4)}
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -461,6 +471,7 @@ def main():
         "kernel_ms": {n: round(per[n], 4) for n in names},
         "events_step_ms": round(step_ms, 4),
         "shader_clock": clk.summary() if clk is not None else None,
+        "at_measured_clock": at_clock(clk.summary() if clk is not None else None, value, fwd_tf, bwd_tf),
         "roofline": {"bound": "mfma", "kernel": kernel_names[dominant], "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dominant) if det or dominant == "fwd" else None},
