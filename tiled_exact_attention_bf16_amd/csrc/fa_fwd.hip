@@ -218,7 +218,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   int n_mine = q0 < Lq ? n_tiles : 0;  // a wave whose rows are all past the end only helps stage K/V
   if constexpr (CAUSAL) n_mine = (q0 >= Lq || q0 + 31 + coff < 0) ? 0 : min(n_tiles, (q0 + 31 + coff) / BN + 1);
 
-  // ---- one pipelined step j: S(j) = K(j) Q^T runs on the matrix cores while the
+  // ---- (one query tile per workgroup, and the key split) one pipelined step j of a
+  // wave: S(j) = K(j) Q^T runs on the matrix cores while the
   // weights of tile j-1 are exponentiated; then O^T += V(j-1)^T P(j-1)^T runs
   // while the row maxima of S(j) are reduced.  Each wave's instruction stream thus
   // alternates matrix and vector work: a few vector instructions issued after an
