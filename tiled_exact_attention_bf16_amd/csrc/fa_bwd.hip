@@ -812,11 +812,16 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      // raised priority: these products issue ahead of the other wave's vector work
+      // on the SIMD, so that the vector work of one wave runs beside the products of
+      // the other more often
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         s = mfma_f16(lds_read16(kt + 32 * kb * ROWB + off_r[ds]), qreg[ds], s);
         dp = mfma_bf16(lds_read16(vt + 32 * kb * ROWB + off_r[ds]), doreg[ds], dp);
       }
+      __builtin_amdgcn_s_setprio(0);
       u32x4 dsh[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
