@@ -162,9 +162,13 @@ fa_status fa_fwd(const fa_fwd_args* a, const fa_fwd_tuning* tuning, void* worksp
  * `workspace` (the first step of fa_fwd for variable length; fdeinterviews.com FA4
  * summary, features paragraph: tiles are dispatched most expensive first), so that
  * it can be inspected.  Layout: int32 count n, then n pairs {sequence, query tile},
- * tiles of `fa_fwd_tile_rows` rows, in dispatch order, cost (key tiles visited)
- * non-increasing; items of equal cost may come in any order.  Errors as fa_fwd,
- * plus FA_ERR_INVALID_ARGUMENT for a fixed-length `a`. */
+ * tiles of `fa_fwd_tile_rows` rows, in dispatch order.  Longest first by cost
+ * bucket: with cost = key tiles visited (64 keys each) and bucket = cost / w,
+ * w = 16 * tile_rows / 64, the bucket never increases along the list; inside a
+ * bucket each sequence's items form one run of non-increasing cost (the runs of
+ * different sequences may come in any order), so that neighbouring tiles of one
+ * sequence run together and share its K/V in L2.  Errors as fa_fwd, plus
+ * FA_ERR_INVALID_ARGUMENT for a fixed-length `a`. */
 fa_status fa_fwd_build_schedule(const fa_fwd_args* a, const fa_fwd_tuning* tuning,
                                 void* workspace, size_t workspace_bytes, void* stream);
 

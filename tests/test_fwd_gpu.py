@@ -170,7 +170,7 @@ def test_config_c4_every_sequence():
     check_heads(inp, o, lse, [(b, h) for b in seqs for h in range(1, 15)], tag="c4 other heads", strict=True)
 
 
-def test_longest_first_schedule_c4():
+def test_grouped_longest_first_schedule_c4():
     inp = named_inputs("c4")
     q, k, _, _, cu = upload(inp)
     for qt in (1, 2):
@@ -181,7 +181,7 @@ def test_longest_first_schedule_c4():
                 for b in range(len(lens)) for t in range(-(-int(lens[b]) // tile_rows))}
         items = [(b, t, c) for (b, t), c in cost.items()]
         got = [(b, t, cost[(b, t)]) for b, t in order]
-        assert OS.is_longest_first(got, items)
+        assert OS.is_grouped_longest_first(got, items, OS.bucket_width(tile_rows, 64))
         say(f"[schedule] tile_rows={tile_rows} items={len(order)} first cost {got[0][2]} last cost {got[-1][2]}")
 
 

@@ -113,3 +113,53 @@ def test_longest_first_order_validity():
     assert SCH.is_longest_first(order, items)
     assert not SCH.is_longest_first(items, items)          # natural order increases cost
     assert not SCH.is_longest_first(order[:-1], items)     # an item is missing
+
+
+def test_grouped_order_hand_example():
+    # causal, 128-row items against 64-key tiles: lengths 300 and 1000 give costs
+    # (2, 4, 5) and (2, 4, 6, ..., 16); buckets of width 4 (two items' growth)
+    items = SCH.work_items([300, 1000], 128, 64, causal=True)
+    assert SCH.bucket_width(128, 64, group=2) == 4
+    order = SCH.grouped_longest_first(items, 4)
+    assert [(b, t) for b, t, _ in order] == [(1, 7), (1, 6), (1, 5), (1, 4), (1, 3),
+                                             (0, 2), (0, 1), (1, 2), (1, 1), (0, 0), (1, 0)]
+    assert SCH.is_grouped_longest_first(order, items, 4)
+    # the other sequence's run first inside a bucket is as valid
+    alt = order[:5] + order[7:9] + order[5:7] + order[9:]
+    assert SCH.is_grouped_longest_first(alt, items, 4)
+
+
+def test_grouped_order_rejections():
+    items = SCH.work_items([300, 1000], 128, 64, causal=True)
+    cost = {(b, t): c for b, t, c in items}
+    mk = lambda bt: [(b, t, cost[(b, t)]) for b, t in bt]
+    good = [(1, 7), (1, 6), (1, 5), (1, 4), (1, 3), (0, 2), (0, 1), (1, 2), (1, 1), (0, 0), (1, 0)]
+    assert SCH.is_grouped_longest_first(mk(good), items, 4)
+    # sequence 0's run in bucket 1 interrupted by sequence 1
+    split = good[:5] + [(0, 2), (1, 2), (0, 1), (1, 1)] + good[9:]
+    assert not SCH.is_grouped_longest_first(mk(split), items, 4)
+    # cost rising inside a run (12 before 14 in bucket 3)
+    rising = good[:1] + [(1, 5), (1, 6)] + good[3:]
+    assert not SCH.is_grouped_longest_first(mk(rising), items, 4)
+    # the most expensive bucket last
+    assert not SCH.is_grouped_longest_first(mk(good[1:] + good[:1]), items, 4)
+    assert not SCH.is_grouped_longest_first(mk(good[:-1]), items, 4)   # an item missing
+    assert not SCH.is_grouped_longest_first(items, items, 4)           # natural order
+    # with wider buckets the strict longest-first order interleaves the sequences
+    many = SCH.work_items([300, 5, 1000, 129, 700], 128, 64, causal=True)
+    assert not SCH.is_grouped_longest_first(SCH.longest_first(many), many, 8)
+
+
+def test_grouped_order_is_valid_for_random_lengths():
+    import random
+    rnd = random.Random(3)
+    for _ in range(50):
+        lens = [rnd.randint(1, 3000) for _ in range(rnd.randint(1, 9))]
+        for causal in (False, True):
+            items = SCH.work_items(lens, 256, 64, causal)
+            w = SCH.bucket_width(256, 64)
+            order = SCH.grouped_longest_first(items, w)
+            assert SCH.is_grouped_longest_first(order, items, w)
+            # bucket order refines the strict one: costs never rise by a bucket or more
+            costs = [c for _, _, c in order]
+            assert all(b - a < w for a, b in zip(costs, costs[1:]) if b > a)

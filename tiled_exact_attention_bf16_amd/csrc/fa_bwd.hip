@@ -914,10 +914,21 @@ __global__ __launch_bounds__(1024) void sched_kv_kernel(const int32_t* cu_q, con
     const int first = causal ? max(0, j * kBwdBlockN - (lk - lq)) / kBwdBlockM : 0;
     return min(max(steps - first, 0), kSchedMaxCost);
   };
+  // Longest first by cost bucket: a bucket spans the cost change of 16 neighbouring
+  // causal key blocks, and within a bucket each sequence's blocks stay together, longest
+  // first, so that the workgroups running at one time read the same sequences' Q and
+  // dO and find them in L2
+  constexpr int bw = 16 * kBwdBlockN / kBwdBlockM;
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
     const int lk = cu_k[b + 1] - cu_k[b];
     const int nb = (lk + kBwdBlockN - 1) / kBwdBlockN;
-    for (int j = 0; j < nb; ++j) atomicAdd(&hist[cost_of(b, j)], 1);
+    for (int j = 0; j < nb;) {
+      const int bk = cost_of(b, j) / bw;
+      int j1 = j + 1;
+      while (j1 < nb && cost_of(b, j1) / bw == bk) ++j1;
+      atomicAdd(&hist[bk], j1 - j);
+      j = j1;
+    }
     atomicAdd(&total, nb);
   }
   __syncthreads();
@@ -926,10 +937,16 @@ __global__ __launch_bounds__(1024) void sched_kv_kernel(const int32_t* cu_q, con
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
     const int lk = cu_k[b + 1] - cu_k[b];
     const int nb = (lk + kBwdBlockN - 1) / kBwdBlockN;
-    for (int j = 0; j < nb; ++j) {
-      const int pos = atomicAdd(&hist[cost_of(b, j)], 1);
-      out[1 + 2 * pos] = b;
-      out[2 + 2 * pos] = j;
+    for (int j = 0; j < nb;) {
+      const int bk = cost_of(b, j) / bw;
+      int j1 = j + 1;
+      while (j1 < nb && cost_of(b, j1) / bw == bk) ++j1;
+      int pos = atomicAdd(&hist[bk], j1 - j);
+      for (int u = j; u < j1; ++u, ++pos) {
+        out[1 + 2 * pos] = b;
+        out[2 + 2 * pos] = u;
+      }
+      j = j1;
     }
   }
 }

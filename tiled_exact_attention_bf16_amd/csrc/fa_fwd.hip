@@ -832,10 +832,21 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const 
     if (causal) kv = max(0, min(lk, min(lq, (t + 1) * tile_rows) + lk - lq));
     return min((kv + block_n - 1) / block_n, kSchedMaxCost);
   };
+  // Longest first by cost bucket: a bucket spans the cost growth of 16 consecutive
+  // causal tiles (16 * tile_rows keys), and within a bucket each sequence's tiles stay
+  // together, longest first, so that the workgroups running at one time read the same
+  // sequences' K/V and find it in L2
+  const int bw = max(1, 16 * tile_rows / block_n);
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
     const int lq = cu_q[b + 1] - cu_q[b];
     const int nt = (lq + tile_rows - 1) / tile_rows;
-    for (int t = 0; t < nt; ++t) atomicAdd(&hist[cost_of(b, t)], 1);
+    for (int t = 0; t < nt;) {
+      const int bk = cost_of(b, t) / bw;
+      int t1 = t + 1;
+      while (t1 < nt && cost_of(b, t1) / bw == bk) ++t1;
+      atomicAdd(&hist[bk], t1 - t);
+      t = t1;
+    }
     atomicAdd(&total, nt);
   }
   __syncthreads();
@@ -844,10 +855,16 @@ __global__ __launch_bounds__(1024) void sched_kernel(const int32_t* cu_q, const 
   for (int b = threadIdx.x; b < batch; b += blockDim.x) {
     const int lq = cu_q[b + 1] - cu_q[b];
     const int nt = (lq + tile_rows - 1) / tile_rows;
-    for (int t = 0; t < nt; ++t) {
-      const int pos = atomicAdd(&hist[cost_of(b, t)], 1);
-      out[1 + 2 * pos] = b;
-      out[2 + 2 * pos] = t;
+    for (int t = 0; t < nt;) {
+      const int bk = cost_of(b, t) / bw;
+      int t1 = t + 1;
+      while (t1 < nt && cost_of(b, t1) / bw == bk) ++t1;
+      int pos = atomicAdd(&hist[bk], t1 - t);
+      for (int u = t1 - 1; u >= t; --u, ++pos) {
+        out[1 + 2 * pos] = b;
+        out[2 + 2 * pos] = u;
+      }
+      t = t1;
     }
   }
 }
