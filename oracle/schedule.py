@@ -15,11 +15,12 @@ Any order whose costs never increase is a valid longest-first order (equal costs
 may come in any order), so checks compare the multiset of items and the cost
 sequence, and verify monotonicity.
 
-The pages do not fix the granularity of "longest first".  The library reads it at
-the granularity of cost buckets (the grouped order below): items whose costs fall
-in the same bucket of ``width`` cost units are equally long for dispatch, buckets
-go most expensive first, and inside a bucket each sequence's items stay together,
-longest first, so that neighbouring tiles of one sequence run at the same time.
+The pages do not fix the granularity at which items go most expensive first.  The
+library reads it at the granularity of cost buckets (the grouped order below): items
+whose costs fall in the same bucket of ``width`` cost units are equally long for
+dispatch, buckets go most expensive first, and inside a bucket each sequence's items
+stay together, longest first, so that neighbouring tiles of one sequence run at the
+same time.
 """
 from __future__ import annotations
 
