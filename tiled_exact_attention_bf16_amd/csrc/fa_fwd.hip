@@ -675,14 +675,24 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       }
     if (hl == 0 && my_row < Lq) p.part_lse[slot + my_row] = lse;
   } else {
+    // lane l and lane l+32 hold the same row's columns 32db+8q4+0..3 and +4..7: one
+    // swap of the halves per pair of q4 gives every lane 8 consecutive columns (lane l
+    // those of q4 = 2k, lane l+32 those of 2k+1), stored with one 16-byte write
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * hl;
-        const u32x2 w = {pack_bf16(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
-                         pack_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
-        buf_store8(ro, (uint32_t)my_row * o_ss2 + d * 2, w);
+      for (int k = 0; k < 2; ++k) {
+        uint32_t a[2], b[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          a[e] = pack_bf16(oacc[db][8 * k + 2 * e] * inv, oacc[db][8 * k + 2 * e + 1] * inv);
+          b[e] = pack_bf16(oacc[db][8 * k + 4 + 2 * e] * inv, oacc[db][8 * k + 4 + 2 * e + 1] * inv);
+          const auto r = __builtin_amdgcn_permlane32_swap(a[e], b[e], false, false);
+          a[e] = r[0];
+          b[e] = r[1];
+        }
+        const int d = 32 * db + 16 * k + 8 * hl;
+        buf_store16(ro, (uint32_t)my_row * o_ss2 + d * 2, u32x4{a[0], a[1], b[0], b[1]});
       }
     if (hl == 0 && my_row < Lq) p.lse[lseoff + my_row] = lse;
   }
