@@ -192,8 +192,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc)
     int h = 0;
     int64_t row = 0;
     if (live) {
-      h = (int)(rh / p.total_q);
-      row = rh - (int64_t)h * p.total_q;
+      // rows in memory order (the head inside the row), so that a wave reads contiguous bytes
+      row = rh / p.heads;
+      h = (int)(rh - row * p.heads);
       const u32x4 ov = *(const u32x4*)((const uint16_t*)p.o + offs(row, h, p.o_sb, p.o_ss, p.o_sh, p.seqlen_q) + chunk * 8);
       const u32x4 dv = *(const u32x4*)((const uint16_t*)p.dout + offs(row, h, p.do_sb, p.do_ss, p.do_sh, p.seqlen_q) + chunk * 8);
       const u32x4 qv = *(const u32x4*)((const uint16_t*)p.q + offs(row, h, p.q_sb, p.q_ss, p.q_sh, p.seqlen_q) + chunk * 8);
@@ -221,8 +222,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc)
     float sq = 0.0f;
     const bool live = rh < total_krows;
     if (live) {
-      const int h = (int)(rh / p.total_k);
-      const int64_t row = rh - (int64_t)h * p.total_k;
+      const int64_t row = rh / p.heads;
+      const int h = (int)(rh - row * p.heads);
       const u32x4 kv = *(const u32x4*)((const uint16_t*)p.k + offs(row, h, p.k_sb, p.k_ss, p.k_sh, p.seqlen_k) + chunk * 8);
       const u32x4 vv = *(const u32x4*)((const uint16_t*)p.v + offs(row, h, p.v_sb, p.v_ss, p.v_sh, p.seqlen_k) + chunk * 8);
       kmax = max(kmax, max_mag8(kv));
