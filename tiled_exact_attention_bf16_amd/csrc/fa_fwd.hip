@@ -718,7 +718,9 @@ __global__ __launch_bounds__(256) void vprep_kernel(FwdParams p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int PER = BN * CPR / 256;      // chunks per thread
   __shared__ uint32_t wmax[4];
-  const int t = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
+  // heads fastest: neighbouring workgroups read the same rows of V (all heads of a row
+  // are adjacent in memory)
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   int Lk = p.seqlen_k;
   int64_t voff, krow0;
   if constexpr (VARLEN) {
@@ -769,7 +771,7 @@ __global__ __launch_bounds__(256) void vprep_kernel(FwdParams p) {
 hipError_t launch_fwd_vprep(const FwdParams& p, int head_dim, bool varlen, hipStream_t stream) {
   const int tiles = (p.seqlen_k + kFwdBlockN - 1) / kFwdBlockN;  // seqlen_k: the longest key sequence
   if (tiles == 0 || p.batch == 0) return hipSuccess;
-  const dim3 grid((unsigned)tiles, (unsigned)p.batch, (unsigned)p.heads);
+  const dim3 grid((unsigned)p.heads, (unsigned)tiles, (unsigned)p.batch);
   if (head_dim == 128) {
     if (varlen) hipLaunchKernelGGL((vprep_kernel<128, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((vprep_kernel<128, false>), grid, dim3(256), 0, stream, p);
