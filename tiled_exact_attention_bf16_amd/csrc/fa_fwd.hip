@@ -418,8 +418,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // same SIMDs (wave w and wave w+4 share one), form the weights of their last
     // scores.  The lead tile (waves 0-3) runs M(m) in slot 2m and V(m) in slot 2m+1;
     // the lag tile runs V(m-1) in slot 2m and M(m) in slot 2m+1.  K(m+1) and V(m) are
-    // loaded from slot 2m on and waited for at the barrier that opens slot 2m+2;
-    // K(j) sits in K buffer j&1, V(j) in V buffer j&1. ----
+    // loaded by the lead tile's waves during slot 2m and waited for at the barrier
+    // that opens slot 2m+2; K(j) sits in K buffer j&1, V(j) in V buffer j&1. ----
     const bool lead = (wave >> 2) == 0;
     f32x16 s[NKB];      // S(j) of the tile in hand
     u32x4 pb[2 * NKB];  // its fp16 weights, the B operand of the next PV product
@@ -427,9 +427,43 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // matrix slot of tile j: S(j) = K(j) Q^T (DS) and O^T += V(j-1)^T P(j-1)^T (DPV).
     // The wave's priority is raised so that its MFMAs issue as soon as the matrix
     // core is free.
-    auto mphase = [&](auto par_c, auto ds_c, auto dpv_c) __attribute__((always_inline)) {
+    // Step m's loads (K(m+1), V(m)) are issued by the lead tile's waves, one 1 KiB
+    // packet after every second MFMA of their matrix slot.  Issued by all eight waves
+    // at the step's opening they queued at the CU's address unit (~15 cycles per
+    // packet), and the waves that issued last started their slot ~480 cycles late.
+    // Part u of a lead wave's share is packet wave + 4 (u % PPL) of K (u < PPL) or of
+    // V.  Past the last tile the last tile is loaded again, into the buffer that no
+    // product reads any more, so that the issue needs no branch.
+    constexpr int PPL = TILE_BYTES / 1024 / 4;  // packets of a tile per lead wave
+    constexpr int NPART = 2 * PPL;
+    static_assert(PPL * 4 * 1024 == TILE_BYTES, "whole packets per lead wave");
+    // A wave's packets wave + 4k start 256k / SLOTS rows apart, a multiple of 16, and
+    // the slot swizzle depends on the row mod 16 only: each lane's offset is one
+    // register per tensor plus a wave-uniform row term.
+    static_assert((256 / SLOTS) % 16 == 0, "the packets of a wave share the swizzle");
+    const int l_row = (wave * 64 + lane) / SLOTS;
+    const int l_cs = ((wave * 64 + lane) % SLOTS) ^ slot_swizzle<D>(l_row);
+    const uint32_t k_lane = (uint32_t)l_row * k_ss2 + l_cs * 16, v_lane = (uint32_t)l_row * v_ss2 + l_cs * 16;
+    auto dma_part = [&](const int m, auto par_c, const int u) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_c)::value;
+      const int k = u % PPL;
+      if (u < PPL) {
+        const int t = max(0, min(m + 1, n_tiles - 1));
+        buf_load_lds16(rk, kbuf(P ^ 1) + (wave + 4 * k) * 1024, k_lane + (uint32_t)(t * BN + k * (256 / SLOTS)) * k_ss2);
+      } else {
+        const int t = max(0, min(m, n_tiles - 1));
+        buf_load_lds16(rv, vbuf(P) + (wave + 4 * k) * 1024, v_lane + (uint32_t)(t * BN + k * (256 / SLOTS)) * v_ss2);
+      }
+      dma_issued();
+    };
+    auto mphase = [&](auto par_c, auto ds_c, auto dpv_c, auto dma_c, const int m) __attribute__((always_inline)) {
       constexpr int P = decltype(par_c)::value;  // j & 1
       constexpr bool DS = decltype(ds_c)::value, DPV = decltype(dpv_c)::value;
+      constexpr bool DMA = decltype(dma_c)::value;  // this wave issues step m's loads
+      if constexpr (DMA && !(DS || DPV)) {
+#pragma unroll
+        for (int u = 0; u < NPART; ++u) dma_part(m, par_c, u);
+      }
       const FA_LDS char* kt = kbuf(P);
       const FA_LDS char* vt = vbuf(P ^ 1);
       if constexpr (DS || DPV) __builtin_amdgcn_s_setprio(1);
@@ -451,14 +485,19 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
           const u32x2 hi = lds_read_tr16(vt + 16 * g * ROWB + off_v2[db]);
           oacc[db] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[g], oacc[db]);
         }
+        if constexpr (DMA && (DS || DPV)) {
+          if (i < NPART) dma_part(m, par_c, i);
+        }
       }
       if constexpr (DS || DPV) {
-        // operand reads run a few MFMAs ahead
+        // operand reads run a few MFMAs ahead; the loads go out one per loop step
         constexpr int NMF = (DS ? NKB * NDS : 0) + (DPV ? (BN / 16) * NDB : 0);
+        constexpr int PER = NMF / (NKB * NDS);  // MFMAs per loop step
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (DMA && i % PER == PER - 1 && i / PER < NPART) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -534,14 +573,13 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       }
       lsum_r += (wsum[0] + wsum[1]) * __int_as_float((127 - e_cur) << 23);
     };
-    // opening of step m (slot 2m): wait for the loads issued at slot 2m-2, barrier,
-    // start K(m+1) and V(m)
-    auto open_step = [&](const int m, auto par_c) __attribute__((always_inline)) {
-      constexpr int P = decltype(par_c)::value;
+    // opening of step m (slot 2m): wait for the loads issued in slot 2m-2, barrier.
+    // The barrier between the two slots of a step orders no memory (the loads in
+    // flight fill buffers that neither slot reads): a bare s_barrier, at which no wave
+    // waits for its loads.
+    auto open_step = [&]() __attribute__((always_inline)) {
       wait_vmem();
       __syncthreads();
-      if (m + 1 < n_tiles) issue(rk, k_ss2, m + 1, kbuf(P ^ 1));
-      if (m < n_tiles) issue(rv, v_ss2, m, vbuf(P));
     };
     // Steps come in kinds fixed at compile time (which products and weights a wave
     // has in them, whether the tile needs the mask), run from straight-line
@@ -549,17 +587,17 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // copy the accumulators between the paths.
     auto lead_step = [&](const int m, auto par_c, auto ds_c, auto dpv_c, auto v_c, auto mask_c)
                          __attribute__((always_inline)) {
-      open_step(m, par_c);
-      mphase(par_c, ds_c, dpv_c);
-      __syncthreads();
+      open_step();
+      mphase(par_c, ds_c, dpv_c, std::true_type{}, m);
+      __builtin_amdgcn_s_barrier();
       if constexpr (decltype(v_c)::value) vphase(m, mask_c);
     };
     auto lag_step = [&](const int m, auto par_c, auto v_c, auto mask_c, auto ds_c, auto dpv_c)
                         __attribute__((always_inline)) {
-      open_step(m, par_c);
+      open_step();
       if constexpr (decltype(v_c)::value) vphase(m - 1, mask_c);
-      __syncthreads();
-      mphase(par_c, ds_c, dpv_c);
+      __builtin_amdgcn_s_barrier();
+      mphase(par_c, ds_c, dpv_c, std::false_type{}, m);
     };
     // A wave with n = n_mine tiles: step 0 has S(0) and (lead) its weights; steps
     // 1..n-1 have everything; step n has PV(n-1) (and, lag, the weights of n-1);
