@@ -774,6 +774,23 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     dma_issued();
   };
 
+  // part u of this wave's share of tile t's loads: packet wave + NW (u % PPW) of K
+  // (u < PPW) or of V; the packets of a wave start a multiple of 16 rows apart, so
+  // that each lane's offset is one register per tensor plus a wave-uniform row term
+  constexpr int PPW = TILE_BYTES / 1024 / NW;
+  constexpr int NPART = 2 * PPW;
+  static_assert(PPW * NW * 1024 == TILE_BYTES && (NW * 64 / SLOTS) % 16 == 0, "packet layout");
+  const int l_row = (wave * 64 + lane) / SLOTS;
+  const int l_cs = ((wave * 64 + lane) % SLOTS) ^ slot_swizzle<D>(l_row);
+  const uint32_t k_lane = (uint32_t)l_row * k_ss2 + l_cs * 16, v_lane = (uint32_t)l_row * v_ss2 + l_cs * 16;
+  auto dma_part = [&](const int t, const int stage, const int u) __attribute__((always_inline)) {
+    const int k = u % PPW;
+    const uint32_t row = (uint32_t)(t * BN + k * (NW * 64 / SLOTS));
+    if (u < PPW) buf_load_lds16(rk, kbuf(stage) + (wave + NW * k) * 1024, k_lane + row * k_ss2);
+    else buf_load_lds16(rv, vbuf(stage) + (wave + NW * k) * 1024, v_lane + row * v_ss2);
+    dma_issued();
+  };
+
   // lane-constant LDS offsets within a tile: with the stage a compile-time constant
   // every operand read is one register plus an immediate
   const int sw_row = slot_swizzle<D>(lane & 15);
@@ -802,7 +819,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     constexpr bool MASK = decltype(mask_c)::value;
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(t + 1, STAGE ^ 1);
+    // tile t+1's loads go out one packet per two MFMAs of the first score block
+    // (issued together at the barrier they queue at the CU's address unit); past the
+    // last tile the last tile is loaded again into the free stage, without a branch
+    const int t_next = min(t + 1, n_tiles - 1);
     const int k0 = t * BN;
     const FA_LDS char* kt = kbuf(STAGE);
     const FA_LDS char* vt = vbuf(STAGE);
@@ -821,6 +841,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       for (int ds = 0; ds < NDS; ++ds) {
         s = mfma_f16(lds_read16(kt + 32 * kb * ROWB + off_r[ds]), qreg[ds], s);
         dp = mfma_bf16(lds_read16(vt + 32 * kb * ROWB + off_r[ds]), doreg[ds], dp);
+        if (kb == 0 && ds * NPART / NDS * NDS == ds * NPART) dma_part(t_next, STAGE ^ 1, ds * NPART / NDS);
       }
       __builtin_amdgcn_s_setprio(0);
       u32x4 dsh[2];
@@ -882,6 +903,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(t + 1, (t & 1) ^ 1);
   }
+  wait_vmem();  // the last tile's repeated loads land before the LDS is released
 
   const float qs = pow2f(ex.f + ex.b);  // the accumulators hold dQ 2^-(f+b)
   const int gb = p.grad_bf16 ? 2 : 4;

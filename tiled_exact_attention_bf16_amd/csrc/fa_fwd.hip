@@ -657,6 +657,9 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
         else lag_step(m, I0{}, BF{}, MF{}, BF{}, BF{});
       }
     }
+    // the last steps' loads (the last tile again) land before the workgroup's LDS is
+    // released
+    wait_vmem();
   } else {
   f32x16 sa[NKB], sb[NKB];
   if (n_tiles > 0) issue(rk, k_ss2, 0, kbuf(0));
