@@ -507,15 +507,25 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // unrounded weights (plain adds: v_dot2 runs on the matrix pipeline and would wait
     // behind the other wave's MFMAs)
     float wsum[2];
-    auto weights = [&](const float mx_ref) __attribute__((always_inline)) {
+    // hidden keys (the causal diagonal, the ragged last tile): key k0 + 4hl + rel(kb, r)
+    // is hidden when rel >= lim; their weights are 0 and they take no part in the row
+    // maximum (the scores themselves stay as they are: masking them in place kept
+    // both the raw and the masked scores live and made the masked steps spill)
+    auto rel_of = [](const int kb, const int r) { return 32 * kb + 8 * (r >> 2) + (r & 3); };
+    auto weights = [&](const float mx_ref, auto mask_c, const int lim) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
       wsum[0] = wsum[1] = 0.0f;
 #pragma unroll
       for (int q = 0; q < 8 * NKB; ++q) {
         const int kb = q >> 3, u = q & 7, e = 2 * u;
         const float x0 = __builtin_fmaf(s[kb][e], c, -mx_ref);
         const float x1 = __builtin_fmaf(s[kb][e + 1], c, -mx_ref);
-        const float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
-        const float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
+        float p0 = (e < POLY) ? exp2_poly(x0) : exp2_hw(x0);
+        float p1 = (e + 1 < POLY) ? exp2_poly(x1) : exp2_hw(x1);
+        if constexpr (MASK) {
+          p0 = rel_of(kb, e) >= lim ? 0.0f : p0;
+          p1 = rel_of(kb, e + 1) >= lim ? 0.0f : p1;
+        }
         pb[2 * kb + (u >> 2)][u & 3] = pack_f16(p0, p1);
         wsum[q & 1] += p0 + p1;
       }
@@ -528,27 +538,25 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
       constexpr bool MASK = decltype(mask_c)::value;
       const int k0 = j * BN;
       const int e_cur = v_exp[k0];  // tile j's V-copy exponent: weights carry 2^e_cur
+      int lim = 0;
       if constexpr (MASK) {
-        int lim = Lk;
+        lim = Lk;
         if constexpr (CAUSAL) lim = min(lim, my_row + 1 + coff);
         lim -= k0 + 4 * hl;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rel = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = rel >= lim ? -INFINITY : s[kb][r];
-          }
       }
-      weights(mref - (float)e_cur);
+      auto sv = [&](const int kb, const int r) {  // score as the row maximum sees it
+        if constexpr (MASK) return rel_of(kb, r) >= lim ? -INFINITY : s[kb][r];
+        else return s[kb][r];
+      };
+      weights(mref - (float)e_cur, mask_c, lim);
       float mp[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kb = t >> 1, r0 = 8 * (t & 1);
-        mp[t] = max3(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2]);
-        mp[t] = max3(mp[t], s[kb][r0 + 3], s[kb][r0 + 4]);
-        mp[t] = max3(mp[t], s[kb][r0 + 5], s[kb][r0 + 6]);
-        mp[t] = fmaxf(mp[t], s[kb][r0 + 7]);
+        mp[t] = max3(sv(kb, r0), sv(kb, r0 + 1), sv(kb, r0 + 2));
+        mp[t] = max3(mp[t], sv(kb, r0 + 3), sv(kb, r0 + 4));
+        mp[t] = max3(mp[t], sv(kb, r0 + 5), sv(kb, r0 + 6));
+        mp[t] = fmaxf(mp[t], sv(kb, r0 + 7));
       }
       float mx = max3(mp[0], mp[1], fmaxf(mp[2], mp[3]));
       mx = half_swap_max(mx);
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        weights(mref - (float)e_cur);
+        weights(mref - (float)e_cur, mask_c, lim);
       }
       lsum_r += (wsum[0] + wsum[1]) * __int_as_float((127 - e_cur) << 23);
     };
