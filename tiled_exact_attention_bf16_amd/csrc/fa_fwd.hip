@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
   // alternates matrix and vector work: a few vector instructions issued after an
   // MFMA run while it executes, and the other wave on the SIMD fills the rest.
   // K(j) sits in K buffer j&1, V(j-1) in V buffer (j-1)&1; the loads of K(j+1) and
-  // V(j) are issued after the barrier that opens step j and waited for at the
+  // V(j) are issued between the MFMAs of phase 1 of step j and waited for at the
   // barrier that opens step j+1.
   auto step = [&](const int j, auto par_c, auto prev_c, auto next_c, auto mask_c, f32x16(&s_prev)[NKB],
                   f32x16(&s_next)[NKB]) {
@@ -235,8 +235,30 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     constexpr bool MASK = decltype(mask_c)::value;  // tile j may hold keys this wave must not see
     wait_vmem();
     __syncthreads();
-    if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(PAR ^ 1));
-    if (j < n_tiles) issue(rv, v_ss2, j, vbuf(PAR));
+    // this wave's packets of K(j+1) and V(j) (the last tile again past the end, into
+    // the buffer no product reads any more): part u is packet wave + NW (u % PW) of K
+    // (u < PW) or of V, one after every second MFMA of phase 1
+    constexpr int PW = TILE_BYTES / 1024 / NW;
+    static_assert(PW * NW * 1024 == TILE_BYTES && (NW * 64 / SLOTS) % 16 == 0, "packet layout");
+    auto part = [&](const int u) __attribute__((always_inline)) {
+      const int l_row = (wave * 64 + lane) / SLOTS;
+      const int l_cs = ((wave * 64 + lane) % SLOTS) ^ slot_swizzle<D>(l_row);
+      const int k = u % PW;
+      if (u < PW) {
+        const int t = max(0, min(j + 1, n_tiles - 1));
+        buf_load_lds16(rk, kbuf(PAR ^ 1) + (wave + NW * k) * 1024,
+                       (uint32_t)(t * BN + k * (NW * 64 / SLOTS) + l_row) * k_ss2 + l_cs * 16);
+      } else {
+        const int t = max(0, min(j, n_tiles - 1));
+        buf_load_lds16(rv, vbuf(PAR) + (wave + NW * k) * 1024,
+                       (uint32_t)(t * BN + k * (NW * 64 / SLOTS) + l_row) * v_ss2 + l_cs * 16);
+      }
+      dma_issued();
+    };
+    if constexpr (!NEXT) {
+#pragma unroll
+      for (int u = 0; u < 2 * PW; ++u) part(u);
+    }
     const FA_LDS char* kt = kbuf(PAR);
     const FA_LDS char* vt = vbuf(PAR ^ 1);
     const int k0 = j * BN;
@@ -277,6 +299,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
         if constexpr (NEXT) {
           const u32x4 a = lds_read16(kt + 32 * kb * ROWB + off_k[ds]);
           s_next[kb] = mfma_bf16(a, qreg[ds], s_next[kb]);
+          if ((kb * NDS + ds) % (NKB * NDS / (2 * PW)) == 0) part((kb * NDS + ds) / (NKB * NDS / (2 * PW)));
         }
         if constexpr (PREV) {
 #pragma unroll
@@ -290,6 +313,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < NM1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % (NM1 / (2 * PW)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         if (i < NM1 - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
@@ -701,6 +725,7 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     if (j + 1 < n_tiles) issue(rk, k_ss2, j + 1, kbuf(par ^ 1));
     if (j < n_tiles) issue(rv, v_ss2, j, vbuf(par));
   }
+  wait_vmem();  // the last steps' repeated loads land before the LDS is released
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m*scale + ln l (O_acc and the sums are in
