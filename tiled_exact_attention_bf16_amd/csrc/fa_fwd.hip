@@ -453,8 +453,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     // core is free.
     // Step m's loads (K(m+1), V(m)) are issued by the lead tile's waves, one 1 KiB
     // packet after every second MFMA of their matrix slot.  Issued by all eight waves
-    // at the step's opening they queued at the CU's address unit (~15 cycles per
-    // packet), and the waves that issued last started their slot ~480 cycles late.
+    // at the step's opening, the 32 packets would queue at the CU's address unit (~15
+    // cycles each) and the waves issuing last would start their slot ~480 cycles late.
     // Part u of a lead wave's share is packet wave + 4 (u % PPL) of K (u < PPL) or of
     // V.  Past the last tile the last tile is loaded again, into the buffer that no
     // product reads any more, so that the issue needs no branch.
@@ -533,8 +533,8 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
     float wsum[2];
     // hidden keys (the causal diagonal, the ragged last tile): key k0 + 4hl + rel(kb, r)
     // is hidden when rel >= lim; their weights are 0 and they take no part in the row
-    // maximum (the scores themselves stay as they are: masking them in place kept
-    // both the raw and the masked scores live and made the masked steps spill)
+    // maximum (the scores themselves stay as they are: masking them in place keeps
+    // both the raw and the masked scores live, and the masked steps spill more)
     auto rel_of = [](const int kb, const int r) { return 32 * kb + 8 * (r >> 2) + (r & 3); };
     auto weights = [&](const float mx_ref, auto mask_c, const int lim) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_c)::value;
