@@ -88,6 +88,9 @@ typedef struct fa_fwd_args {
   int32_t total_k;
   float softmax_scale;   /* finite and > 0, e.g. 1/sqrt(D); else see fa_fwd       */
   int32_t causal;        /* 0 or 1                                                 */
+  int32_t o_dtype;       /* FA_DTYPE_BF16 (0, the default) or FA_DTYPE_F32: O in fp32,
+                            the normalised output before its bf16 rounding (a
+                            diagnostic; o_stride then counts fp32 elements)          */
 } fa_fwd_args;
 
 /* Optional forward variant selection (NULL = defaults).  The knobs select among
@@ -143,8 +146,9 @@ fa_status fa_fwd_workspace_size(const fa_fwd_args* a, const fa_fwd_tuning* tunin
  * contents ignored on entry and clobbered) may be NULL when that size is 0.
  * Errors, all reported before any device work is enqueued:
  *   FA_ERR_INVALID_ARGUMENT  NULL or misaligned pointer, negative size, stride
- *                            smaller than head_dim or not a multiple of 8
- *                            elements, causal not 0/1, non-finite scale;
+ *                            smaller than head_dim or not a multiple of 16
+ *                            bytes, causal not 0/1, o_dtype not BF16/F32,
+ *                            non-finite scale;
  *   FA_ERR_UNSUPPORTED       head_dim not 64/128, scale <= 0 (the kernels fold
  *                            the scale into the exponent after taking row maxima
  *                            of the raw scores, which needs a positive scale),

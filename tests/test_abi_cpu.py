@@ -110,6 +110,24 @@ def test_forward_validation(mutate, expect):
     assert ws_size(a)[0] == expect
 
 
+def test_fp32_output_option():
+    # o_dtype selects bf16 (default) or fp32 O; anything else is rejected before any
+    # device work, and fp32 strides count fp32 elements (multiples of 4 for 16 bytes)
+    a = fwd_args()
+    a.o_dtype = 2
+    assert fwd_status(a) == L.FA_ERR_INVALID_ARGUMENT
+    assert ws_size(a)[0] == L.FA_ERR_INVALID_ARGUMENT
+    a = fwd_args()
+    a.o_dtype = L.FA_DTYPE_F32
+    a.o_stride = L.Strides(256 * 4 * 132, 4 * 132, 132)
+    assert ws_size(a) == (L.FA_OK, v16_bytes(4, 2 * 256, 128))
+    a.o_stride = L.Strides(256 * 4 * 130, 4 * 130, 130)   # 520 bytes: not a 16-byte multiple
+    assert ws_size(a)[0] == L.FA_ERR_INVALID_ARGUMENT
+    b = fwd_args()                                         # the same strides in bf16 elements
+    b.o_stride = L.Strides(256 * 4 * 132, 4 * 132, 132)   # 264 bytes: not a 16-byte multiple
+    assert ws_size(b)[0] == L.FA_ERR_INVALID_ARGUMENT
+
+
 @pytest.mark.parametrize("tuning,expect", [
     ((3, -1, -1), L.FA_ERR_UNSUPPORTED),
     ((2, 0, -1), L.FA_ERR_UNSUPPORTED),

@@ -201,6 +201,32 @@ def test_output_canaries_and_strided_views():
     check_heads(inp, o_view, lse_view, [(b, h) for b in range(2) for h in range(3)], tag="strided")
 
 
+@pytest.mark.parametrize("case", ["fixed_full", "fixed_causal", "varlen_causal", "key_split"])
+def test_fp32_output_is_the_unrounded_output(case):
+    """An fp32 O is the normalised output before its bf16 rounding: rounded to bf16 (RNE)
+    it equals the bf16 O of the same call bit for bit, the LSE is the same, and it meets
+    the bar against the oracle."""
+    tuning = None
+    if case == "varlen_causal":
+        inp = I.random_varlen_inputs(911, [1, 300, 64, 0, 1000], 3, 128, True)
+    elif case == "key_split":
+        inp = I.random_inputs(913, 2, 7, 4, 128, True, seqlen_k=5000)
+        tuning = FA.Tuning(key_splits=4)
+    else:
+        inp = I.random_inputs(917, 2, 700, 3, 128, case == "fixed_causal")
+    say(f"case fp32 O {case}")
+    q, k, v, _, cu = upload(inp)
+    kw = dict(cu_seqlens_q=cu, max_seqlen_q=inp.max_seqlen() if inp.varlen else None, tuning=tuning)
+    o16, lse16 = FA.fwd(q, k, v, inp.scale, inp.causal, **kw)
+    o32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _, lse32 = FA.fwd(q, k, v, inp.scale, inp.causal, out=o32, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(lse32, lse16)
+    pairs = [(0, 0), (inp.batch - 1, inp.num_heads - 1)]
+    check_heads(inp, o32, lse32, pairs, tag=f"fp32 O {case}", strict=True)
+
+
 def test_forward_is_bitwise_repeatable():
     inp = I.random_inputs(31, 2, 2048, 4, 128, True, q_std=3.0)
     q, k, v, _, _ = upload(inp)

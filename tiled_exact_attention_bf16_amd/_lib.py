@@ -47,7 +47,7 @@ class FwdArgs(ctypes.Structure):
         ("head_dim", c_int32),
         ("cu_seqlens_q", c_void_p), ("cu_seqlens_k", c_void_p),
         ("max_seqlen_q", c_int32), ("max_seqlen_k", c_int32), ("total_q", c_int32), ("total_k", c_int32),
-        ("softmax_scale", c_float), ("causal", c_int32),
+        ("softmax_scale", c_float), ("causal", c_int32), ("o_dtype", c_int32),
     ]
 
 

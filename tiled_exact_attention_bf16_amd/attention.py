@@ -134,6 +134,7 @@ def fwd_args(q, k, v, o, lse, softmax_scale, causal, cu_seqlens_q=None, cu_seqle
     a.num_heads, a.head_dim = q.shape[-2], q.shape[-1]
     a.softmax_scale = softmax_scale
     a.causal = int(bool(causal))
+    a.o_dtype = L.FA_DTYPE_F32 if o.dtype == torch.float32 else L.FA_DTYPE_BF16
     if varlen:
         a.batch = cu_seqlens_q.numel() - 1
         a.cu_seqlens_q = _ptr(cu_seqlens_q)
@@ -155,13 +156,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: Option
         max_seqlen_k: Optional[int] = None, tuning: Optional[Tuning] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Exact attention forward.  Returns (O bf16 like q, LSE fp32 [B,H,S] or [H,T])."""
+    """Exact attention forward.  Returns (O bf16 like q, LSE fp32 [B,H,S] or [H,T]).  An
+    fp32 `out` receives the normalised output before its bf16 rounding (a diagnostic)."""
     _check_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     varlen = cu_seqlens_q is not None
     if out is not None:
-        _check_tensor("out", out, torch.bfloat16, q.shape)
+        _check_tensor("out", out, torch.float32 if out.dtype == torch.float32 else torch.bfloat16, q.shape)
     if lse is not None:
         _check_lse(lse, q, varlen)
     _check_workspace(workspace)

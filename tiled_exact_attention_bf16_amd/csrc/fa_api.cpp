@@ -132,7 +132,8 @@ fa_status check_fwd(const fa_fwd_args* a, Shape* s) {
   if ((st = check_tensor(a->q, a->q_stride, *s, s->max_q, 2)) != FA_OK) return st;
   if ((st = check_tensor(a->k, a->k_stride, *s, s->max_k, 2)) != FA_OK) return st;
   if ((st = check_tensor(a->v, a->v_stride, *s, s->max_k, 2)) != FA_OK) return st;
-  if ((st = check_tensor(a->o, a->o_stride, *s, s->max_q, 2)) != FA_OK) return st;
+  if (a->o_dtype != FA_DTYPE_BF16 && a->o_dtype != FA_DTYPE_F32) return FA_ERR_INVALID_ARGUMENT;
+  if ((st = check_tensor(a->o, a->o_stride, *s, s->max_q, a->o_dtype == FA_DTYPE_F32 ? 4 : 2)) != FA_OK) return st;
   if (a->lse == nullptr || ((uintptr_t)a->lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
   return FA_OK;
 }
@@ -189,6 +190,7 @@ fa::FwdParams make_fwd_params(const fa_fwd_args* a, const Shape& s) {
   p.k_sb = a->k_stride[0]; p.k_ss = a->k_stride[1]; p.k_sh = a->k_stride[2];
   p.v_sb = a->v_stride[0]; p.v_ss = a->v_stride[1]; p.v_sh = a->v_stride[2];
   p.o_sb = a->o_stride[0]; p.o_ss = a->o_stride[1]; p.o_sh = a->o_stride[2];
+  p.o_f32 = a->o_dtype == FA_DTYPE_F32 ? 1 : 0;
   p.batch = s.batch;
   p.seqlen_q = s.max_q;
   p.seqlen_k = s.max_k;

@@ -748,6 +748,19 @@ __global__ __launch_bounds__(256 * NQT, 2) void fwd_kernel(FwdParams p) {
                           __float_as_uint(oacc[db][4 * q4 + 2] * inv), __float_as_uint(oacc[db][4 * q4 + 3] * inv)});
       }
     if (hl == 0 && my_row < Lq) p.part_lse[slot + my_row] = lse;
+  } else if (p.o_f32) {
+    // fp32 O (a diagnostic): four consecutive columns per 16-byte write
+    const rsrc_t ro32 = make_rsrc((char*)p.o + ooff * 4, (uint32_t)(Lq - 1) * (uint32_t)(p.o_ss * 4) + D * 4);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * db + 8 * q4 + 4 * hl;
+        buf_store16(ro32, (uint32_t)my_row * (uint32_t)(p.o_ss * 4) + d * 4,
+                    u32x4{__float_as_uint(oacc[db][4 * q4 + 0] * inv), __float_as_uint(oacc[db][4 * q4 + 1] * inv),
+                          __float_as_uint(oacc[db][4 * q4 + 2] * inv), __float_as_uint(oacc[db][4 * q4 + 3] * inv)});
+      }
+    if (hl == 0 && my_row < Lq) p.lse[lseoff + my_row] = lse;
   } else {
     // lane l and lane l+32 hold the same row's columns 32db+8q4+0..3 and +4..7: one
     // swap of the halves per pair of q4 gives every lane 8 consecutive columns (lane l
@@ -896,7 +909,8 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
     ooff = (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh;
     lidx = ((int64_t)b * p.heads + h) * p.seqlen_q + i;
   }
-  *(u32x2*)((uint16_t*)p.o + ooff + d) = u32x2{pack_bf16(o0 * inv, o1 * inv), pack_bf16(o2 * inv, o3 * inv)};
+  if (p.o_f32) *(f32x4*)((float*)p.o + ooff + d) = f32x4{o0 * inv, o1 * inv, o2 * inv, o3 * inv};
+  else *(u32x2*)((uint16_t*)p.o + ooff + d) = u32x2{pack_bf16(o0 * inv, o1 * inv), pack_bf16(o2 * inv, o3 * inv)};
   if (d == 0) p.lse[lidx] = wsum > 0.0f ? m + __logf(wsum) : -INFINITY;
 }
 

@@ -25,6 +25,7 @@ struct FwdParams {
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
+  int o_f32;           // O is fp32 (strides in fp32 elements), else bf16
   int batch, seqlen_q, seqlen_k, heads;
   const int32_t* cu_q;
   const int32_t* cu_k;
