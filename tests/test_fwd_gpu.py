@@ -201,7 +201,7 @@ def test_output_canaries_and_strided_views():
     check_heads(inp, o_view, lse_view, [(b, h) for b in range(2) for h in range(3)], tag="strided")
 
 
-@pytest.mark.parametrize("case", ["fixed_full", "fixed_causal", "varlen_causal", "key_split"])
+@pytest.mark.parametrize("case", ["fixed_full", "fixed_causal", "fixed_causal_d64", "varlen_causal", "key_split"])
 def test_fp32_output_is_the_unrounded_output(case):
     """An fp32 O is the normalised output before its bf16 rounding: rounded to bf16 (RNE)
     it equals the bf16 O of the same call bit for bit, the LSE is the same, and it meets
@@ -213,7 +213,7 @@ def test_fp32_output_is_the_unrounded_output(case):
         inp = I.random_inputs(913, 2, 7, 4, 128, True, seqlen_k=5000)
         tuning = FA.Tuning(key_splits=4)
     else:
-        inp = I.random_inputs(917, 2, 700, 3, 128, case == "fixed_causal")
+        inp = I.random_inputs(917, 2, 700, 3, 64 if case.endswith("d64") else 128, case.startswith("fixed_causal"))
     say(f"case fp32 O {case}")
     q, k, v, _, cu = upload(inp)
     kw = dict(cu_seqlens_q=cu, max_seqlen_q=inp.max_seqlen() if inp.varlen else None, tuning=tuning)
