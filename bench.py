@@ -404,7 +404,7 @@ def main():
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the driver refreshes its clock readings only every few hundred ms and a short
+    # the amdgpu kernel driver refreshes its clock readings only every few hundred ms and a short
     # timed region can end before one shows the busy clock: keep running the same step
     # outside the timed region until three busy readings have arrived, for at most 4 s
     if clk is not None:
