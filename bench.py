@@ -65,7 +65,8 @@ def recorded_traffic(phase: str):
 class ClockSampler:
     """Shader clock while the kernels run: amdsmi's current GFX clock of each of the
     GPU's XCDs (gpu metrics), polled every 5 ms by a background thread; each new
-    reading (the driver refreshes them far less often than that) counts once, and
+    reading (the amdgpu kernel driver refreshes them far less often than that) counts
+    once, and
     readings of an idle GPU (below 500 MHz, deep sleep) are dropped.  None without
     amdsmi."""
 
@@ -404,8 +405,8 @@ def main():
         e[4].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the amdgpu kernel driver refreshes its clock readings only every few hundred ms and a short
-    # timed region can end before one shows the busy clock: keep running the same step
+    # the amdgpu kernel driver refreshes its clock readings only every few hundred ms, and
+    # a short timed region can end before one shows the busy clock: keep running the same step
     # outside the timed region until three busy readings have arrived, for at most 4 s
     if clk is not None:
         t1 = time.perf_counter()
