@@ -66,8 +66,7 @@ class ClockSampler:
     """Shader clock while the kernels run: amdsmi's current GFX clock of each of the
     GPU's XCDs (gpu metrics), polled every 5 ms by a background thread; each new
     reading (the amdgpu kernel driver refreshes them far less often than that) counts
-    once, and
-    readings of an idle GPU (below 500 MHz, deep sleep) are dropped.  None without
+    once, and readings of an idle GPU (below 500 MHz, deep sleep) are dropped.  None without
     amdsmi."""
 
     def __init__(self):
