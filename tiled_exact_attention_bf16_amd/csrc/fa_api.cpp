@@ -138,9 +138,11 @@ fa_status check_fwd(const fa_fwd_args* a, Shape* s) {
   return FA_OK;
 }
 
-// Key chunks for the split forward: more workgroups when the query tiles alone
-// (at 128 rows) leave the GPU short of work and every chunk still spans at least
-// 16 key tiles of 64.
+// Key chunks for the split forward, when the query tiles alone (at 128 rows) leave
+// the GPU short of work: about 512 workgroups in all (two per compute unit; more
+// chunks only add per-chunk start, store and merge costs to a pass bound by reading K
+// and V), each chunk spanning at least 32 key tiles of 64 — 16 where chunks that long
+// would leave fewer workgroups than compute units.
 int fwd_key_splits(const Shape& s, const FwdChoice& c) {
   if (c.splits > 0) return c.splits;
   const int64_t items = (int64_t)(s.varlen ? fwd_max_items(s, fa::kFwdTileRows)
@@ -148,8 +150,9 @@ int fwd_key_splits(const Shape& s, const FwdChoice& c) {
                         s.heads;
   const int key_tiles = (s.max_k + fa::kFwdBlockN - 1) / fa::kFwdBlockN;
   if (items >= 512 || key_tiles < 32) return 1;
-  const int want = (int)((1024 + items - 1) / items);
-  return std::max(1, std::min({want, key_tiles / 16, kMaxKeySplits}));
+  const int want = (int)((512 + items - 1) / items);
+  const int longest = items * (key_tiles / 32) >= 256 ? key_tiles / 32 : key_tiles / 16;
+  return std::max(1, std::min({want, longest, kMaxKeySplits}));
 }
 
 // Forward workspace: [work list (variable length)] [partial LSE] [partial O]
