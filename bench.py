@@ -334,6 +334,9 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="only run forward+backward of this named workload (c1..c5, c2_causal, headline) "
                          "--steps times and print per-phase averages (for profiling)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the generation shapes (short queries against 16K keys, with the "
+                         "automatic key split and without a split) and print them (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch a plain device copy of a known size (for scaling HBM counters)")
     args = ap.parse_args()
@@ -354,6 +357,9 @@ def main():
     L.lib()  # fail loudly if the HIP library is missing
     if args.workload:
         run_workload(args.workload, args.steps, args.warmup, not args.atomic, args.tau)
+        return
+    if args.decode_only:
+        print(json.dumps({"decode": time_decode()}), flush=True)
         return
 
     inp = I.make_inputs(BWD_SEED_CONFIG)   # B=2 S=8192 H=16 d=128 causal, with dO
