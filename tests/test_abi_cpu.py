@@ -244,6 +244,29 @@ def test_key_split_workspace_and_validation():
     assert ws_size(big) == (L.FA_OK, v16_bytes(4, 512, 128))
 
 
+@pytest.mark.parametrize("b,h,lq,lk,expect", [
+    (4, 16, 1, 16384, 8),     # 64 items of 128 rows: ~512 workgroups, chunks of 32 tiles
+    (1, 16, 1, 65536, 32),    # 16 items: 32 chunks of 32 tiles
+    (16, 16, 1, 4096, 2),     # 256 items: two chunks
+    (8, 8, 128, 8192, 4),     # capped at 32 key tiles per chunk
+    (1, 8, 64, 4096, 4),      # 8 items: chunks of 16 tiles, as 32-tile chunks leave the GPU idle
+    (4, 16, 1, 2048, 2),      # 32 key tiles: two 16-tile chunks
+    (4, 16, 1, 1984, 1),      # fewer than 32 key tiles: no split
+    (32, 16, 1, 16384, 1),    # 512 items: no split
+])
+def test_automatic_key_split_count(b, h, lq, lk, expect):
+    # the automatic choice shows in the workspace size, which holds one partial O and
+    # LSE per chunk: it equals the size for the expected explicit count
+    a = fwd_args(b=b, s=256, h=h, d=128)
+    a.seqlen_q, a.seqlen_k = lq, lk
+    st, n_auto = ws_size(a)
+    assert st == L.FA_OK
+    assert ws_size(a, L.FwdTuning(-1, -1, -1, expect)) == (L.FA_OK, n_auto)
+    for other in (expect - 1, expect + 1):
+        if 1 <= other <= 64:
+            assert ws_size(a, L.FwdTuning(-1, -1, -1, other))[1] != n_auto
+
+
 def test_causal_with_unequal_lengths_is_accepted():
     # the causal mask aligns the diagonal to the bottom-right corner, so L_q != L_k is valid
     a = fwd_args()
